@@ -1,0 +1,248 @@
+// iqk_dequant.hip -- dequantization of canonical IQ_K streams (the prefill
+// weight producer).  "mlx-iqk" package description, "Format" section: every
+// weight is rebuilt as a float32 chain in the CPU dequantizer's order,
+//   2-bit:    w = (float(d) * float(scale_index)) * values[4*alphabet + code]
+//   IQ1_S_R4: w = (float(d) * float(2*ls + 1)) * (float(grid_value) + shift)
+// and, for half-precision outputs, rounded once to nearest-even.  The
+// introduction states that the producer "dequantizes the stacked experts in
+// one kernel pass" at the streaming floor.
+//
+// The path is write-bound (2 or 4 output bytes per 0.19-0.30 input bytes), so
+// the design keeps every wave store a contiguous 1 KiB run: one item = 16
+// output bytes (8 weights for f16/bf16, 4 for f32), consecutive lanes take
+// consecutive items, and the grid strides over items.  Per-item field loads
+// (a 2-byte code word, 1-byte scale/alphabet words, the fp16 scale) hit L1/L2
+// after the first lane of a sub-block.  This file is compiled without FMA
+// contraction; every multiply rounds on its own.
+#include "iqk_internal.h"
+
+namespace iqk {
+namespace {
+
+constexpr int kThreads = 256;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void store16_nt(void* base, int64_t item, u32x4 v) {
+    __builtin_nontemporal_store(v, (u32x4*)base + item);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// One item = 16 bytes of output; W weights per item.
+template <int OUT_DT>
+struct ItemShape {
+    static constexpr int W = OUT_DT == IQK_F32 ? 4 : 8;
+};
+
+// The float32 product must be rounded to float32 before the half cast; left
+// alone, the compiler folds fptrunc(fmul) into v_fma_mix*_f16, which rounds
+// the exact product once, straight to f16.  An empty asm pins the float32
+// value in a VGPR.
+__device__ __forceinline__ float pin_f32(float v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t pack2(float a, float b, int out_dt) {
+    if (out_dt == IQK_F16) {
+        a = pin_f32(a);
+        b = pin_f32(b);
+        uint16_t ua = __builtin_bit_cast(uint16_t, (_Float16)a);
+        uint16_t ub = __builtin_bit_cast(uint16_t, (_Float16)b);
+        return (uint32_t)ua | ((uint32_t)ub << 16);
+    }
+    uint16_t ua = __builtin_bit_cast(uint16_t, (__bf16)a);
+    uint16_t ub = __builtin_bit_cast(uint16_t, (__bf16)b);
+    return (uint32_t)ua | ((uint32_t)ub << 16);
+}
+
+template <int OUT_DT>
+__device__ __forceinline__ void store_item(void* out, int64_t item, const float* w) {
+    u32x4 v;
+    if constexpr (OUT_DT == IQK_F32) {
+        v.x = __float_as_uint(w[0]);
+        v.y = __float_as_uint(w[1]);
+        v.z = __float_as_uint(w[2]);
+        v.w = __float_as_uint(w[3]);
+    } else {
+        v.x = pack2(w[0], w[1], OUT_DT);
+        v.y = pack2(w[2], w[3], OUT_DT);
+        v.z = pack2(w[4], w[5], OUT_DT);
+        v.w = pack2(w[6], w[7], OUT_DT);
+    }
+    store16_nt(out, item, v);
+}
+
+// Raw field words of one item (the floor variant folds these into its stores).
+struct ItemFields {
+    uint32_t q;      // codes (2-bit members) or low index byte (IQ1_S_R4)
+    uint32_t s0;     // scale word
+    uint32_t s1;     // second scale / alphabet word
+    uint32_t s2;     // alphabet word
+    uint16_t d;      // fp16 scale
+};
+
+template <int FMT, int W>
+__device__ __forceinline__ ItemFields load_item(const uint8_t* __restrict__ S, const Planes& pl, int64_t R, int64_t n,
+                                                int64_t row, int64_t k0) {
+    ItemFields f;
+    if constexpr (FMT == IQK_IQ2_KS) {
+        const int64_t sb = k0 / 32;
+        const uint8_t* qs = S + pl.off[0] + row * (n / 4) + k0 / 4;
+        f.q = W == 8 ? (uint32_t)*(const uint16_t*)qs : (uint32_t)*qs;
+        f.s0 = S[pl.off[1] + row * (n / 64) + sb / 2];
+        f.s1 = S[pl.off[2] + row * (n / 256) + sb / 8];
+        f.s2 = S[pl.off[3] + row * (n / 256) + sb / 8];
+        f.d = *(const uint16_t*)(S + pl.off[4] + 2 * row);
+    } else if constexpr (FMT == IQK_IQ2_K) {
+        const int64_t sb = k0 / 16;
+        const uint8_t* qs = S + pl.off[0] + row * (n / 4) + k0 / 4;
+        f.q = W == 8 ? (uint32_t)*(const uint16_t*)qs : (uint32_t)*qs;
+        f.s0 = S[pl.off[1] + row * (n / 32) + sb / 2];
+        f.s1 = 0;
+        f.s2 = S[pl.off[2] + row * (n / 128) + sb / 8];
+        f.d = *(const uint16_t*)(S + pl.off[3] + 2 * (row * (n / 256) + k0 / 256));
+    } else {
+        f.q = S[pl.off[0] + row * (n / 8) + k0 / 8];
+        f.s0 = *(const uint16_t*)(S + pl.off[1] + 2 * (row * (n / 32) + k0 / 32));
+        f.s1 = 0;
+        f.s2 = 0;
+        f.d = *(const uint16_t*)(S + pl.off[2] + 2 * row);
+    }
+    (void)R;
+    return f;
+}
+
+struct DequantParams {
+    const uint8_t* streams;
+    Planes pl;
+    int64_t R, n, row0, nrows;
+    int64_t ipr;                  // items per row
+    int64_t step_row, step_col;   // grid stride split as rows * ipr + cols
+    float values[8];
+    const int8_t* grid;
+    void* out;
+};
+
+template <int FMT, int OUT_DT, bool FLOOR>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(DequantParams p) {
+    constexpr int W = ItemShape<OUT_DT>::W;
+    __shared__ float tab[8];
+    if (threadIdx.x < 8) tab[threadIdx.x] = p.values[threadIdx.x];
+    __syncthreads();
+
+    const int64_t ipr = p.ipr;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t it = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    // (lr, col) walk the items without a per-item division
+    int64_t lr = it / ipr;
+    int64_t col = it - lr * ipr;
+    for (; lr < p.nrows; it += stride, lr += p.step_row, col += p.step_col) {
+        if (col >= ipr) {
+            col -= ipr;
+            lr += 1;
+            if (lr >= p.nrows) break;
+        }
+        const int64_t k0 = col * W;
+        const int64_t row = p.row0 + lr;
+        ItemFields f = load_item<FMT, W>(p.streams, p.pl, p.R, p.n, row, k0);
+        float w[W];
+        if constexpr (FLOOR) {
+            // deleted decode: the loaded words reach the stores unchanged
+            const uint32_t h = f.q ^ (f.s0 << 8) ^ (f.s1 << 16) ^ (f.s2 << 24) ^ ((uint32_t)f.d << 5);
+#pragma unroll
+            for (int i = 0; i < W; ++i) w[i] = __uint_as_float(h + (uint32_t)i);
+            if constexpr (OUT_DT != IQK_F32) {
+                u32x4 v = {h, h ^ 1u, h ^ 2u, h ^ 3u};
+                store16_nt(p.out, it, v);
+                continue;
+            }
+        } else if constexpr (FMT == IQK_IQ2_KS) {
+            const int sb = (int)((k0 / 32) & 7);
+            const uint32_t lo = (f.s0 >> (4 * (sb & 1))) & 15u;
+            const uint32_t hi = (f.s1 >> sb) & 1u;
+            const int si = (int)(lo | (hi << 4)) - 16;
+            const uint32_t alph = (f.s2 >> sb) & 1u;
+            const float dl = half_bits_to_float(f.d) * (float)si;
+#pragma unroll
+            for (int i = 0; i < W; ++i) w[i] = dl * tab[4 * alph + ((f.q >> (2 * i)) & 3u)];
+        } else if constexpr (FMT == IQK_IQ2_K) {
+            const int sb = (int)((k0 / 16) & 7);
+            const int si = (int)((f.s0 >> (4 * (sb & 1))) & 15u) - 8;
+            const uint32_t alph = (f.s2 >> sb) & 1u;
+            const float dl = half_bits_to_float(f.d) * (float)si;
+#pragma unroll
+            for (int i = 0; i < W; ++i) w[i] = dl * tab[4 * alph + ((f.q >> (2 * i)) & 3u)];
+        } else {
+            const int j = (int)((k0 / 8) & 3);
+            const uint32_t idx = f.q | (((f.s0 >> (3 * j)) & 7u) << 8);
+            const uint32_t ls = (f.s0 >> 12) & 7u;
+            const float shift = (f.s0 >> 15) ? -0.125f : 0.125f;
+            const float scale = half_bits_to_float(f.d) * (float)(2 * ls + 1);
+            const int8_t* g = p.grid + 8 * idx + (k0 & 7);
+            if constexpr (W == 8) {
+                const uint2 gv = *(const uint2*)g;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = scale * ((float)(int8_t)(gv.x >> (8 * i)) + shift);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[4 + i] = scale * ((float)(int8_t)(gv.y >> (8 * i)) + shift);
+            } else {
+                const uint32_t gv = *(const uint32_t*)g;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = scale * ((float)(int8_t)(gv >> (8 * i)) + shift);
+            }
+        }
+        store_item<OUT_DT>(p.out, it, w);
+    }
+}
+
+template <int FMT, int OUT_DT, bool FLOOR>
+hipError_t launch_one(DequantParams p, hipStream_t s) {
+    constexpr int W = ItemShape<OUT_DT>::W;
+    p.ipr = p.n / W;
+    const int64_t items = p.nrows * p.ipr;
+    int64_t blocks = (items + kThreads - 1) / kThreads;
+    // enough workgroups to fill 256 CUs many times over; the grid strides
+    blocks = blocks < 256 * 32 ? blocks : 256 * 32;
+    if (blocks < 1) blocks = 1;
+    const int64_t stride = blocks * kThreads;
+    p.step_row = stride / p.ipr;
+    p.step_col = stride % p.ipr;
+    hipLaunchKernelGGL((dequant_kernel<FMT, OUT_DT, FLOOR>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int FMT, bool FLOOR>
+hipError_t launch_fmt(const DequantParams& p, int out_dt, hipStream_t s) {
+    if (out_dt == IQK_F32) return launch_one<FMT, IQK_F32, FLOOR>(p, s);
+    if (out_dt == IQK_F16) return launch_one<FMT, IQK_F16, FLOOR>(p, s);
+    return launch_one<FMT, IQK_BF16, FLOOR>(p, s);
+}
+
+template <bool FLOOR>
+hipError_t launch_any(const DequantParams& p, int fmt, int out_dt, hipStream_t s) {
+    if (fmt == IQK_IQ2_KS) return launch_fmt<IQK_IQ2_KS, FLOOR>(p, out_dt, s);
+    if (fmt == IQK_IQ2_K) return launch_fmt<IQK_IQ2_K, FLOOR>(p, out_dt, s);
+    return launch_fmt<IQK_IQ1_S_R4, FLOOR>(p, out_dt, s);
+}
+
+}  // namespace
+
+hipError_t launch_dequant(const DequantLaunch& a, bool floor_variant, hipStream_t s) {
+    DequantParams p;
+    p.streams = a.streams;
+    p.pl = a.pl;
+    p.R = a.R;
+    p.n = a.n;
+    p.row0 = a.row0;
+    p.nrows = a.nrows;
+    for (int i = 0; i < 8; ++i) p.values[i] = a.values[i];
+    p.grid = a.grid;
+    p.out = a.out;
+    return floor_variant ? launch_any<true>(p, a.fmt, a.out_dtype, s) : launch_any<false>(p, a.fmt, a.out_dtype, s);
+}
+
+}  // namespace iqk

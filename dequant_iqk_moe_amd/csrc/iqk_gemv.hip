@@ -1,0 +1,479 @@
+// iqk_gemv.hip -- fused dequantize-and-matvec for routed-expert decode.
+//
+// "mlx-iqk" package description:
+//   - "Surface": a call with few token-expert pairs runs a fused decode
+//     matvec; one pass over the reduction axis per instance, so only
+//     instantiated input widths are accepted;
+//   - introduction: codes are read from one contiguous 2-bit plane, the
+//     8-entry value table is held in a narrow type and each sub-block's
+//     alphabet is taken once per sub-block, not once per weight;
+//   - "Format": the stream tables and the two reconstruction formulas.
+//
+// gfx950 design.  The matvec is bound by HBM bytes, but at 8 TB/s the
+// vector ALUs have only ~1.3-1.5 lane-instructions per weight, so the decode
+// must be integer and 4-wide:
+//   * each lane owns 64 consecutive k of a row (one 16-byte load of the code
+//     plane); a wave covers 4096 k per load instruction (1 row at in=4096,
+//     2 rows at 2048, 8 rows at 512), every load coalesced along k;
+//   * the activation is converted once per workgroup to 15-bit fixed point
+//     per 64-value block (scale 2^(13 - emax)), split into two int8 planes
+//     (hi, lo) in LDS, then held by each lane in 32 VGPRs for all its rows;
+//   * 2-bit members: (q >> 2j) & 0x03030303 spreads four codes into four
+//     bytes, OR-ing 4 * alphabet makes each byte an index into the 8-entry
+//     int8 table, and one v_perm_b32 looks up four weights; v_dot4_i32_i8
+//     against the hi and lo planes accumulates exact int32 per sub-block,
+//     v_mad_i32_i24 applies the signed scale index.  The fixed-point x is
+//     pre-permuted in LDS to match the spread order, so no weight moves;
+//   * IQ1_S_R4: the 2048 x 8 int8 grid is staged in LDS (16 KiB); each
+//     8-weight group is one ds_read_b64 and four v_dot4_i32_i8, the +-1/8
+//     shift is applied through the block sum of x;
+//   * per-lane partials of 4 rows are reduced with v_permlane32_swap,
+//     v_permlane16_swap and DPP (10 instructions per 4 rows).
+// Rows are wave-contiguous so the small per-row planes share cache lines
+// inside one workgroup.  Result: y[t, j, o] in float32.
+#include "iqk_internal.h"
+
+namespace iqk {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+struct GemvParams {
+    const uint8_t* S;
+    int64_t off0, off1, off2, off3, off4;
+    int32_t E, out;
+    uint32_t tab_lo, tab_hi;
+    float tab_scale;
+    const int8_t* grid;
+    const void* x;
+    int32_t x_slots, k;
+    const int32_t* ids;
+    float* y;
+    uint32_t* sink;
+    int32_t nrb;      // row blocks per pair
+    int32_t groups;   // reduction groups per wave
+    int32_t rows_wg;  // rows per workgroup
+};
+
+template <int N>
+struct Geo {
+    static constexpr int LPR = N / 64;                                // lanes per row
+    static constexpr int RPI = 64 / LPR;                              // rows per wave iteration
+    static constexpr int GIT = LPR == 64 ? 4 : (LPR == 32 ? 2 : 1);   // iterations per reduction group
+    static constexpr int RPG = GIT * RPI;                             // rows per reduction group
+};
+
+__device__ __forceinline__ float half_to_float(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) { return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) { return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t dpp_half_mirror(uint32_t v) { return __builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t dpp_mirror(uint32_t v) { return __builtin_amdgcn_update_dpp(0u, v, 0x140, 0xF, 0xF, false); }
+
+// Addition on the carried 32-bit values: float for results, integer for the
+// floor variant's accumulator.
+template <bool INT>
+__device__ __forceinline__ uint32_t add32(uint32_t a, uint32_t b) {
+    if constexpr (INT) return a + b;
+    else return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+}
+
+// Sum within each 16-lane row (xor 1, xor 2, half-mirror, mirror): every
+// lane of the row ends with the row's total.
+template <bool INT>
+__device__ __forceinline__ uint32_t reduce16(uint32_t v) {
+    v = add32<INT>(v, dpp_xor1(v));
+    v = add32<INT>(v, dpp_xor2(v));
+    v = add32<INT>(v, dpp_half_mirror(v));
+    v = add32<INT>(v, dpp_mirror(v));
+    return v;
+}
+
+template <bool INT>
+__device__ __forceinline__ uint32_t reduce8(uint32_t v) {
+    v = add32<INT>(v, dpp_xor1(v));
+    v = add32<INT>(v, dpp_xor2(v));
+    v = add32<INT>(v, dpp_half_mirror(v));
+    return v;
+}
+
+// Reduce the GIT per-lane partials of one reduction group.  Returns the sum
+// for the row this lane reports (row index within the group in *row_out),
+// and whether this lane writes it.
+template <int N, bool INT>
+__device__ __forceinline__ uint32_t reduce_group(const uint32_t* part, int lane, int* row_out, bool* writer) {
+    using G = Geo<N>;
+    if constexpr (G::LPR == 64) {
+        // part[i] = row i (all 64 lanes).  32-swap: rows {0,2} and {1,3}
+        auto a = __builtin_amdgcn_permlane32_swap(part[0], part[2], false, false);
+        auto b = __builtin_amdgcn_permlane32_swap(part[1], part[3], false, false);
+        uint32_t u = add32<INT>(a[0], a[1]);  // lanes 0-31: row 0, lanes 32-63: row 2
+        uint32_t v = add32<INT>(b[0], b[1]);  // lanes 0-31: row 1, lanes 32-63: row 3
+        auto c = __builtin_amdgcn_permlane16_swap(u, v, false, false);
+        uint32_t w = add32<INT>(c[0], c[1]);  // 16-lane row g holds row g
+        w = reduce16<INT>(w);
+        *row_out = lane >> 4;
+        *writer = (lane & 15) == 0;
+        return w;
+    } else if constexpr (G::LPR == 32) {
+        // part[i]: lanes 0-31 row 2i, lanes 32-63 row 2i+1
+        auto c = __builtin_amdgcn_permlane16_swap(part[0], part[1], false, false);
+        uint32_t w = add32<INT>(c[0], c[1]);  // 16-lane rows 0..3 hold rows 0, 2, 1, 3
+        w = reduce16<INT>(w);
+        const int g = lane >> 4;
+        *row_out = ((g & 1) << 1) | (g >> 1);
+        *writer = (lane & 15) == 0;
+        return w;
+    } else {
+        // LPR == 8: part[0] lane l belongs to row l / 8
+        uint32_t w = reduce8<INT>(part[0]);
+        *row_out = lane >> 3;
+        *writer = (lane & 7) == 0;
+        return w;
+    }
+}
+
+// Activation in LDS: per 64-value chunk, 64 hi bytes and 64 lo bytes in the
+// order the decode consumes them, plus the chunk scale (and for IQ1_S_R4 the
+// sums of the fixed-point values over each 32-weight block).
+template <int N>
+struct XLds {
+    uint32_t hi[N / 4];
+    uint32_t lo[N / 4];
+    float scale[N / 64];
+    int32_t bsum[N / 32];
+};
+
+// Convert 16 activation values (one 16-block of a chunk) per thread.
+template <int FMT, int N, int XDT>
+__device__ __forceinline__ void prep_x(const void* xrow, XLds<N>& L, int tid) {
+    if (tid >= N / 16) return;
+    float v[16];
+    if constexpr (XDT == IQK_BF16) {
+        const uint4* src = (const uint4*)xrow + 2 * tid;
+        const uint4 a = src[0], b = src[1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    } else {
+        const float4* src = (const float4*)xrow + 4 * tid;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 f = src[i];
+            v[4 * i] = f.x;
+            v[4 * i + 1] = f.y;
+            v[4 * i + 2] = f.z;
+            v[4 * i + 3] = f.w;
+        }
+    }
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = max(amax, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+    // chunk = 4 consecutive threads
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+    int emax = (int)(amax >> 23) - 127;
+    emax = emax < -100 ? -100 : emax;
+    const float s = __builtin_ldexpf(1.0f, 13 - emax);
+    int hi[16], lo[16], q[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        q[i] = (int)__builtin_rintf(v[i] * s);  // |q| <= 2^14
+        hi[i] = (q[i] + 128) >> 8;
+        lo[i] = q[i] - (hi[i] << 8);
+    }
+    uint32_t wh[4], wl[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        // 2-bit members: word j = values j, 4+j, 8+j, 12+j (the code-spread order);
+        // IQ1_S_R4: natural order
+        const int i0 = FMT == IQK_IQ1_S_R4 ? 4 * j : j;
+        const int st = FMT == IQK_IQ1_S_R4 ? 1 : 4;
+        wh[j] = (uint32_t)(hi[i0] & 0xFF) | ((uint32_t)(hi[i0 + st] & 0xFF) << 8) |
+                ((uint32_t)(hi[i0 + 2 * st] & 0xFF) << 16) | ((uint32_t)(hi[i0 + 3 * st] & 0xFF) << 24);
+        wl[j] = (uint32_t)(lo[i0] & 0xFF) | ((uint32_t)(lo[i0 + st] & 0xFF) << 8) |
+                ((uint32_t)(lo[i0 + 2 * st] & 0xFF) << 16) | ((uint32_t)(lo[i0 + 3 * st] & 0xFF) << 24);
+    }
+    *(uint4*)&L.hi[4 * tid] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+    *(uint4*)&L.lo[4 * tid] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+    if ((tid & 3) == 0) L.scale[tid >> 2] = __builtin_ldexpf(1.0f, emax - 13);
+    if constexpr (FMT == IQK_IQ1_S_R4) {
+        int sum = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += q[i];
+        sum += __shfl_xor(sum, 1);
+        if ((tid & 1) == 0) L.bsum[tid >> 1] = sum;
+    }
+}
+
+template <int FMT>
+struct RowData {
+    uint4 q;       // codes / low index bytes (IQ1_S_R4 uses q.x, q.y)
+    uint32_t a, b, c, d;
+};
+
+template <int FMT, int N>
+__device__ __forceinline__ RowData<FMT> load_row(const GemvParams& p, int64_t grow, int c) {
+    RowData<FMT> r;
+    const uint8_t* S = p.S;
+    if constexpr (FMT == IQK_IQ2_K) {
+        r.q = *(const uint4*)(S + p.off0 + grow * (N / 4) + 16 * c);
+        r.a = *(const uint16_t*)(S + p.off1 + grow * (N / 32) + 2 * c);
+        r.b = S[p.off2 + grow * (N / 128) + (c >> 1)];
+        r.c = 0;
+        r.d = *(const uint16_t*)(S + p.off3 + grow * (N / 128) + 2 * (c >> 2));
+    } else if constexpr (FMT == IQK_IQ2_KS) {
+        r.q = *(const uint4*)(S + p.off0 + grow * (N / 4) + 16 * c);
+        r.a = S[p.off1 + grow * (N / 64) + c];
+        r.b = S[p.off2 + grow * (N / 256) + (c >> 2)];
+        r.c = S[p.off3 + grow * (N / 256) + (c >> 2)];
+        r.d = *(const uint16_t*)(S + p.off4 + 2 * grow);
+    } else {
+        const uint2 qq = *(const uint2*)(S + p.off0 + grow * (N / 8) + 8 * c);
+        r.q = make_uint4(qq.x, qq.y, 0, 0);
+        r.a = *(const uint32_t*)(S + p.off1 + grow * (N / 16) + 4 * c);
+        r.b = 0;
+        r.c = 0;
+        r.d = *(const uint16_t*)(S + p.off2 + 2 * grow);
+    }
+    return r;
+}
+
+// Dot of one lane's 64 weights with its 64 activations, in units of
+// (fixed-point x) * (int8 table): returns the float partial before the
+// per-lane scale (d * x-chunk scale * table scale) for the 2-bit members,
+// and including d-independent factors for IQ1_S_R4.
+__device__ __forceinline__ int dot16(uint32_t qw, uint32_t m, uint32_t tlo, uint32_t thi, const uint32_t* x4, int acc) {
+    const uint32_t M = 0x03030303u;
+    const uint32_t w0 = __builtin_amdgcn_perm(thi, tlo, (qw & M) | m);
+    const uint32_t w1 = __builtin_amdgcn_perm(thi, tlo, ((qw >> 2) & M) | m);
+    const uint32_t w2 = __builtin_amdgcn_perm(thi, tlo, ((qw >> 4) & M) | m);
+    const uint32_t w3 = __builtin_amdgcn_perm(thi, tlo, ((qw >> 6) & M) | m);
+    acc = __builtin_amdgcn_sdot4((int)w0, (int)x4[0], acc, false);
+    acc = __builtin_amdgcn_sdot4((int)w1, (int)x4[1], acc, false);
+    acc = __builtin_amdgcn_sdot4((int)w2, (int)x4[2], acc, false);
+    acc = __builtin_amdgcn_sdot4((int)w3, (int)x4[3], acc, false);
+    return acc;
+}
+
+template <int FMT>
+__device__ __forceinline__ float row_dot(const RowData<FMT>& r, int c, const uint32_t* xh, const uint32_t* xl,
+                                         const int32_t* bsum, uint32_t tlo, uint32_t thi, const uint2* grid_s) {
+    if constexpr (FMT == IQK_IQ2_K) {
+        const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+        const uint32_t sc = r.a ^ 0x8888u;               // nibble ^ 8 read as signed 4-bit = nibble - 8
+        const uint32_t sx = r.b >> (4 * (c & 1));
+        int ah = 0, al = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)sx, i, 1) & 0x04040404u;
+            const int h = dot16(q[i], m, tlo, thi, xh + 4 * i, 0);
+            const int l = dot16(q[i], m, tlo, thi, xl + 4 * i, 0);
+            const int si = __builtin_amdgcn_sbfe((int)sc, 4 * i, 4);
+            ah += __mul24(h, si);
+            al += __mul24(l, si);
+        }
+        return (float)ah * 256.0f + (float)al;
+    } else if constexpr (FMT == IQK_IQ2_KS) {
+        const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+        const int sh = 2 * (c & 3);
+        const uint32_t schx = ~r.b;                      // high bit flipped: 5-bit field read signed = raw - 16
+        int ah = 0, al = 0;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const uint32_t raw = ((r.a >> (4 * s)) & 15u) | (((schx >> (sh + s)) & 1u) << 4);
+            const int si = __builtin_amdgcn_sbfe((int)raw, 0, 5);
+            const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)r.c, sh + s, 1) & 0x04040404u;
+            int h = dot16(q[2 * s], m, tlo, thi, xh + 8 * s, 0);
+            h = dot16(q[2 * s + 1], m, tlo, thi, xh + 8 * s + 4, h);
+            int l = dot16(q[2 * s], m, tlo, thi, xl + 8 * s, 0);
+            l = dot16(q[2 * s + 1], m, tlo, thi, xl + 8 * s + 4, l);
+            ah += __mul24(h, si);
+            al += __mul24(l, si);
+        }
+        return (float)ah * 256.0f + (float)al;
+    } else {
+        float part = 0.f;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const uint32_t h16 = (r.a >> (16 * b)) & 0xFFFFu;
+            const uint32_t qsw = b == 0 ? r.q.x : r.q.y;
+            int ah = 0, al = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int g = 4 * b + j;
+                const uint32_t idx = ((qsw >> (8 * j)) & 0xFFu) | (((h16 >> (3 * j)) & 7u) << 8);
+                const uint2 gv = grid_s[idx];
+                ah = __builtin_amdgcn_sdot4((int)gv.x, (int)xh[2 * g], ah, false);
+                ah = __builtin_amdgcn_sdot4((int)gv.y, (int)xh[2 * g + 1], ah, false);
+                al = __builtin_amdgcn_sdot4((int)gv.x, (int)xl[2 * g], al, false);
+                al = __builtin_amdgcn_sdot4((int)gv.y, (int)xl[2 * g + 1], al, false);
+            }
+            const float shift = (h16 >> 15) ? -0.125f : 0.125f;
+            const float tb = (float)ah * 256.0f + (float)al + shift * (float)bsum[b];
+            part += tb * (float)(2 * ((h16 >> 12) & 7u) + 1);
+        }
+        return part;
+    }
+}
+
+template <int FMT, int N, int XDT, bool FLOOR>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
+    using G = Geo<N>;
+    __shared__ XLds<N> X;
+    __shared__ uint2 grid_s[FMT == IQK_IQ1_S_R4 ? 2048 : 1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int bid = blockIdx.x;
+    const int pair = bid / p.nrb;
+    const int rb = bid - pair * p.nrb;
+    const int t = pair / p.k;
+    const int j = pair - t * p.k;
+    const int e = p.ids[pair];
+    const int row_begin = rb * p.rows_wg;
+    const int row_end = min(row_begin + p.rows_wg, p.out);
+    const int64_t out_base = (int64_t)pair * p.out;
+
+    if (e < 0 || e >= p.E) {  // invalid id: NaN rows (all-ones in the floor variant)
+        for (int r = row_begin + tid; r < row_end; r += kThreads) {
+            if constexpr (FLOOR) p.sink[out_base + r] = 0xFFFFFFFFu;
+            else p.y[out_base + r] = __builtin_nanf("");
+        }
+        return;
+    }
+
+    const int64_t xoff = ((int64_t)t * p.x_slots + (p.x_slots == 1 ? 0 : j)) * N;
+    const void* xrow = XDT == IQK_BF16 ? (const void*)((const uint16_t*)p.x + xoff) : (const void*)((const float*)p.x + xoff);
+    prep_x<FMT, N, XDT>(xrow, X, tid);
+    if constexpr (FMT == IQK_IQ1_S_R4) {
+        const uint4* src = (const uint4*)p.grid;
+        uint4* dst = (uint4*)grid_s;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[tid + kThreads * i] = src[tid + kThreads * i];
+    }
+    __syncthreads();
+
+    const int c = lane % G::LPR;  // chunk of k owned by this lane
+    uint32_t xh[16], xl[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 a = *(const uint4*)&X.hi[16 * c + 4 * i];
+        const uint4 b = *(const uint4*)&X.lo[16 * c + 4 * i];
+        xh[4 * i] = a.x; xh[4 * i + 1] = a.y; xh[4 * i + 2] = a.z; xh[4 * i + 3] = a.w;
+        xl[4 * i] = b.x; xl[4 * i + 1] = b.y; xl[4 * i + 2] = b.z; xl[4 * i + 3] = b.w;
+    }
+    const float lane_scale = X.scale[c] * p.tab_scale;
+    int32_t bsum[2] = {0, 0};
+    if constexpr (FMT == IQK_IQ1_S_R4) {
+        bsum[0] = X.bsum[2 * c];
+        bsum[1] = X.bsum[2 * c + 1];
+    }
+    const int lane_row = lane / G::LPR;
+    const int64_t e_rows = (int64_t)e * p.out;
+
+    for (int g = 0; g < p.groups; ++g) {
+        const int grp_row0 = row_begin + (wave * p.groups + g) * G::RPG;
+        if (grp_row0 >= row_end) break;
+        RowData<FMT> rd[G::GIT];
+#pragma unroll
+        for (int it = 0; it < G::GIT; ++it) {
+            const int r = min(grp_row0 + it * G::RPI + lane_row, row_end - 1);
+            rd[it] = load_row<FMT, N>(p, e_rows + r, c);
+        }
+        uint32_t part[G::GIT];
+#pragma unroll
+        for (int it = 0; it < G::GIT; ++it) {
+            if constexpr (FLOOR) {
+                part[it] = rd[it].q.x ^ rd[it].q.y ^ rd[it].q.z ^ rd[it].q.w ^ rd[it].a ^ (rd[it].b << 8) ^
+                           (rd[it].c << 16) ^ (rd[it].d << 3) ^ xh[it & 15];
+            } else {
+                const float f = row_dot<FMT>(rd[it], c, xh, xl, bsum, p.tab_lo, p.tab_hi, grid_s);
+                part[it] = __float_as_uint(f * (half_to_float(rd[it].d) * lane_scale));
+            }
+        }
+        int row_in_grp;
+        bool writer;
+        const uint32_t sum = reduce_group<N, FLOOR>(part, lane, &row_in_grp, &writer);
+        const int r = grp_row0 + row_in_grp;
+        if (writer && r < row_end) {
+            if constexpr (FLOOR) p.sink[out_base + r] = sum;
+            else p.y[out_base + r] = __uint_as_float(sum);
+        }
+    }
+}
+
+template <int FMT, int N, int XDT, bool FLOOR>
+hipError_t launch_inst(GemvParams p, int64_t pairs, hipStream_t s) {
+    using G = Geo<N>;
+    // about two workgroups per CU over the whole call, each wave keeping
+    // at least one reduction group
+    int64_t bpp = (512 + pairs - 1) / pairs;
+    int64_t rows = (p.out + bpp - 1) / bpp;
+    int64_t groups = (rows + kWaves * G::RPG - 1) / (kWaves * G::RPG);
+    groups = groups < 1 ? 1 : (groups > 16 ? 16 : groups);
+    p.groups = (int32_t)groups;
+    p.rows_wg = (int32_t)(groups * kWaves * G::RPG);
+    p.nrb = (int32_t)((p.out + p.rows_wg - 1) / p.rows_wg);
+    const int64_t blocks = pairs * p.nrb;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((gemv_kernel<FMT, N, XDT, FLOOR>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int FMT, int N, bool FLOOR>
+hipError_t launch_x(const GemvParams& p, int xdt, int64_t pairs, hipStream_t s) {
+    if (xdt == IQK_BF16) return launch_inst<FMT, N, IQK_BF16, FLOOR>(p, pairs, s);
+    return launch_inst<FMT, N, IQK_F32, FLOOR>(p, pairs, s);
+}
+
+template <int FMT, bool FLOOR>
+hipError_t launch_n(const GemvParams& p, int64_t n, int xdt, int64_t pairs, hipStream_t s) {
+    if (n == 4096) return launch_x<FMT, 4096, FLOOR>(p, xdt, pairs, s);
+    if (n == 2048) return launch_x<FMT, 2048, FLOOR>(p, xdt, pairs, s);
+    return launch_x<FMT, 512, FLOOR>(p, xdt, pairs, s);
+}
+
+template <bool FLOOR>
+hipError_t launch_fmt(const GemvParams& p, int fmt, int64_t n, int xdt, int64_t pairs, hipStream_t s) {
+    if (fmt == IQK_IQ2_KS) return launch_n<IQK_IQ2_KS, FLOOR>(p, n, xdt, pairs, s);
+    if (fmt == IQK_IQ2_K) return launch_n<IQK_IQ2_K, FLOOR>(p, n, xdt, pairs, s);
+    return launch_n<IQK_IQ1_S_R4, FLOOR>(p, n, xdt, pairs, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const GemvLaunch& a, bool floor_variant, hipStream_t s) {
+    GemvParams p;
+    p.S = a.streams;
+    p.off0 = a.pl.off[0];
+    p.off1 = a.pl.off[1];
+    p.off2 = a.pl.off[2];
+    p.off3 = a.pl.off[3];
+    p.off4 = a.pl.off[4];
+    p.E = (int32_t)a.E;
+    p.out = (int32_t)a.out;
+    p.tab_lo = a.tab_lo;
+    p.tab_hi = a.tab_hi;
+    p.tab_scale = a.tab_scale;
+    p.grid = a.grid;
+    p.x = a.x;
+    p.x_slots = a.x_slots;
+    p.k = a.k;
+    p.ids = a.ids;
+    p.y = a.y;
+    p.sink = a.sink;
+    p.nrb = p.groups = p.rows_wg = 0;
+    const int64_t pairs = a.T * a.k;
+    return floor_variant ? launch_fmt<true>(p, a.fmt, a.n, a.x_dtype, pairs, s)
+                         : launch_fmt<false>(p, a.fmt, a.n, a.x_dtype, pairs, s);
+}
+
+}  // namespace iqk

@@ -1,0 +1,498 @@
+// iqk_host.cpp -- C-ABI entry points of the IQ_K routed-expert library:
+// argument validation, the host relayout (wire <-> canonical streams) and
+// dispatch to the HIP kernels.  See include/iqk.h for the contract of every
+// call and the byte layouts.
+#include <algorithm>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "iqk_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt_msg, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt_msg, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt_msg);
+    vsnprintf(buf, sizeof buf, fmt_msg, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return IQK_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+    return fail(IQK_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool known_fmt(int fmt) { return fmt == IQK_IQ2_KS || fmt == IQK_IQ2_K || fmt == IQK_IQ1_S_R4; }
+
+int check_fmt_shape(int fmt, int64_t n) {
+    if (!known_fmt(fmt)) return fail(IQK_E_FORMAT, "unknown format %d", fmt);
+    if (!iqk::shape_ok(fmt, n))
+        return fail(IQK_E_SHAPE, "in_features %lld violates the %s rule", (long long)n,
+                    fmt == IQK_IQ1_S_R4 ? "multiple-of-32" : "multiple-of-256");
+    return IQK_OK;
+}
+
+int check_weights(const iqk_weights* w) {
+    if (!w) return fail(IQK_E_ARG, "null weight descriptor");
+    int rc = check_fmt_shape(w->fmt, w->in);
+    if (rc) return rc;
+    if (w->experts <= 0 || w->out <= 0) return fail(IQK_E_ARG, "experts and out must be positive");
+    if (!w->streams) return fail(IQK_E_ARG, "null stream pointer");
+    const int64_t R = w->experts * w->out;
+    const size_t need = (size_t)(R * iqk::row_bytes(w->fmt, w->in));
+    if (w->streams_bytes != need)
+        return fail(IQK_E_SIZE, "streams_bytes %zu != %zu for %lld rows of %lld", w->streams_bytes, need,
+                    (long long)R, (long long)w->in);
+    return IQK_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Host relayout.  Wire layouts are the stand-in readings of the ik block
+// structs documented in iqk.h; the stream layout is the canonical one.
+// ---------------------------------------------------------------------------
+
+inline uint16_t rd16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+inline void wr16(uint8_t* p, uint16_t v) {
+    p[0] = (uint8_t)v;
+    p[1] = (uint8_t)(v >> 8);
+}
+
+// Codes of one 256-weight block: wire qs[64] (interleaved) <-> k-contiguous
+// qs[64] (weight j at byte j/4, bits 2(j%4)).  Wire weight j = 128h + 32p + l
+// sits in byte 32h + l at bits 2p.
+inline void qs_wire_to_stream(const uint8_t* wq, uint8_t* sq) {
+    for (int m = 0; m < 64; ++m) {
+        const int j0 = 4 * m, h = j0 / 128, p = (j0 % 128) / 32, l0 = j0 % 32;
+        const uint8_t* src = wq + 32 * h + l0;
+        const int sh = 2 * p;
+        sq[m] = (uint8_t)(((src[0] >> sh) & 3) | (((src[1] >> sh) & 3) << 2) | (((src[2] >> sh) & 3) << 4) |
+                          (((src[3] >> sh) & 3) << 6));
+    }
+}
+inline void qs_stream_to_wire(const uint8_t* sq, uint8_t* wq) {
+    std::memset(wq, 0, 64);
+    for (int m = 0; m < 64; ++m) {
+        const int j0 = 4 * m, h = j0 / 128, p = (j0 % 128) / 32, l0 = j0 % 32;
+        uint8_t* dst = wq + 32 * h + l0;
+        const int sh = 2 * p;
+        for (int i = 0; i < 4; ++i) dst[i] |= (uint8_t)(((sq[m] >> (2 * i)) & 3) << sh);
+    }
+}
+
+struct Relayout {
+    int fmt;
+    int64_t R, n;
+    iqk::Planes pl;
+};
+
+// One row (IQ2_*) or one four-row group (IQ1_S_R4), wire -> streams.
+void pack_unit(const Relayout& L, const uint8_t* wire, uint8_t* s, int64_t u) {
+    const int64_t n = L.n, R = L.R;
+    if (L.fmt == IQK_IQ2_KS) {
+        const int64_t r = u;
+        const uint8_t* row = wire + r * iqk::row_bytes(L.fmt, n);
+        uint8_t* qs = s + L.pl.off[0] + r * n / 4;
+        uint8_t* scl = s + L.pl.off[1] + r * n / 64;
+        uint8_t* sch = s + L.pl.off[2] + r * n / 256;
+        uint8_t* sex = s + L.pl.off[3] + r * n / 256;
+        wr16(s + L.pl.off[4] + 2 * r, rd16(row));
+        for (int64_t b = 0; b < n / 256; ++b) {
+            const uint8_t* blk = row + 2 + 70 * b;
+            const uint16_t extra = rd16(blk);
+            sex[b] = (uint8_t)(extra & 0xff);
+            sch[b] = (uint8_t)(extra >> 8);
+            std::memcpy(scl + 4 * b, blk + 2, 4);
+            qs_wire_to_stream(blk + 6, qs + 64 * b);
+        }
+    } else if (L.fmt == IQK_IQ2_K) {
+        const int64_t r = u;
+        const uint8_t* row = wire + r * iqk::row_bytes(L.fmt, n);
+        uint8_t* qs = s + L.pl.off[0] + r * n / 4;
+        uint8_t* scl = s + L.pl.off[1] + r * n / 32;
+        uint8_t* sex = s + L.pl.off[2] + r * n / 128;
+        uint8_t* dv = s + L.pl.off[3] + r * (n / 256) * 2;
+        for (int64_t b = 0; b < n / 256; ++b) {
+            const uint8_t* blk = row + 76 * b;
+            wr16(dv + 2 * b, rd16(blk));
+            wr16(sex + 2 * b, rd16(blk + 2));
+            std::memcpy(scl + 8 * b, blk + 4, 8);
+            qs_wire_to_stream(blk + 12, qs + 64 * b);
+        }
+    } else {
+        const int64_t g = u, rb = iqk::row_bytes(L.fmt, n);
+        const uint8_t* grp = wire + g * 4 * rb;
+        for (int ri = 0; ri < 4; ++ri) {
+            const int64_t r = 4 * g + ri;
+            uint8_t* qs = s + L.pl.off[0] + r * n / 8;
+            uint8_t* qh = s + L.pl.off[1] + r * (n / 32) * 2;
+            wr16(s + L.pl.off[2] + 2 * r, rd16(grp + 2 * ri));
+            for (int64_t b = 0; b < n / 32; ++b) {
+                const uint8_t* blk = grp + 8 + 24 * b;
+                for (int j = 0; j < 4; ++j) qs[4 * b + j] = blk[4 * j + ri];
+                wr16(qh + 2 * b, rd16(blk + 16 + 2 * ri));
+            }
+        }
+    }
+    (void)R;
+}
+
+void unpack_unit(const Relayout& L, const uint8_t* s, uint8_t* wire, int64_t u) {
+    const int64_t n = L.n;
+    if (L.fmt == IQK_IQ2_KS) {
+        const int64_t r = u;
+        uint8_t* row = wire + r * iqk::row_bytes(L.fmt, n);
+        const uint8_t* qs = s + L.pl.off[0] + r * n / 4;
+        const uint8_t* scl = s + L.pl.off[1] + r * n / 64;
+        const uint8_t* sch = s + L.pl.off[2] + r * n / 256;
+        const uint8_t* sex = s + L.pl.off[3] + r * n / 256;
+        wr16(row, rd16(s + L.pl.off[4] + 2 * r));
+        for (int64_t b = 0; b < n / 256; ++b) {
+            uint8_t* blk = row + 2 + 70 * b;
+            wr16(blk, (uint16_t)(sex[b] | (sch[b] << 8)));
+            std::memcpy(blk + 2, scl + 4 * b, 4);
+            qs_stream_to_wire(qs + 64 * b, blk + 6);
+        }
+    } else if (L.fmt == IQK_IQ2_K) {
+        const int64_t r = u;
+        uint8_t* row = wire + r * iqk::row_bytes(L.fmt, n);
+        const uint8_t* qs = s + L.pl.off[0] + r * n / 4;
+        const uint8_t* scl = s + L.pl.off[1] + r * n / 32;
+        const uint8_t* sex = s + L.pl.off[2] + r * n / 128;
+        const uint8_t* dv = s + L.pl.off[3] + r * (n / 256) * 2;
+        for (int64_t b = 0; b < n / 256; ++b) {
+            uint8_t* blk = row + 76 * b;
+            wr16(blk, rd16(dv + 2 * b));
+            wr16(blk + 2, rd16(sex + 2 * b));
+            std::memcpy(blk + 4, scl + 8 * b, 8);
+            qs_stream_to_wire(qs + 64 * b, blk + 12);
+        }
+    } else {
+        const int64_t g = u, rb = iqk::row_bytes(L.fmt, n);
+        uint8_t* grp = wire + g * 4 * rb;
+        for (int ri = 0; ri < 4; ++ri) {
+            const int64_t r = 4 * g + ri;
+            const uint8_t* qs = s + L.pl.off[0] + r * n / 8;
+            const uint8_t* qh = s + L.pl.off[1] + r * (n / 32) * 2;
+            wr16(grp + 2 * ri, rd16(s + L.pl.off[2] + 2 * r));
+            for (int64_t b = 0; b < n / 32; ++b) {
+                uint8_t* blk = grp + 8 + 24 * b;
+                for (int j = 0; j < 4; ++j) blk[4 * j + ri] = qs[4 * b + j];
+                wr16(blk + 16 + 2 * ri, rd16(qh + 2 * b));
+            }
+        }
+    }
+}
+
+template <class F>
+void parallel_units(int64_t units, F&& f) {
+    unsigned hw = std::thread::hardware_concurrency();
+    int64_t nt = std::min<int64_t>(std::max(1u, std::min(hw, 16u)), std::max<int64_t>(1, units / 64));
+    if (nt <= 1) {
+        for (int64_t u = 0; u < units; ++u) f(u);
+        return;
+    }
+    std::vector<std::thread> th;
+    for (int64_t t = 0; t < nt; ++t) {
+        th.emplace_back([&, t] {
+            const int64_t a = units * t / nt, b = units * (t + 1) / nt;
+            for (int64_t u = a; u < b; ++u) f(u);
+        });
+    }
+    for (auto& x : th) x.join();
+}
+
+int check_relayout(int fmt, const void* a, size_t a_bytes, int64_t rows, int64_t n, const void* b, size_t b_bytes) {
+    int rc = check_fmt_shape(fmt, n);
+    if (rc) return rc;
+    if (rows < 0) return fail(IQK_E_ARG, "negative row count");
+    if (fmt == IQK_IQ1_S_R4 && rows % 4) return fail(IQK_E_ROWS4, "IQ1_S_R4 wire needs rows %% 4 == 0 (got %lld)", (long long)rows);
+    const size_t need = (size_t)(rows * iqk::row_bytes(fmt, n));
+    if (a_bytes != need || b_bytes != need)
+        return fail(IQK_E_SIZE, "relayout buffers must hold %zu bytes (got %zu and %zu)", need, a_bytes, b_bytes);
+    if (need && (!a || !b)) return fail(IQK_E_ARG, "null buffer");
+    const uint8_t* pa = (const uint8_t*)a;
+    const uint8_t* pb = (const uint8_t*)b;
+    if (need && pa < pb + need && pb < pa + need) return fail(IQK_E_ARG, "relayout buffers overlap");
+    return IQK_OK;
+}
+
+// Value table -> int8 m_i with values[i] = m_i * 2^e (common e).
+bool table_to_int8(const float* v, uint32_t* lo, uint32_t* hi, float* scale) {
+    int emin = 1 << 30;
+    float amax = 0.f;
+    for (int i = 0; i < 8; ++i) {
+        if (!std::isfinite(v[i])) return false;
+        if (v[i] == 0.f) continue;
+        int ex;
+        double m = std::frexp((double)v[i], &ex);  // v = m * 2^ex, 0.5 <= |m| < 1
+        // lowest set bit of the 24-bit significand
+        int64_t sig = (int64_t)std::ldexp(std::fabs(m), 24);
+        int tz = 0;
+        while ((sig & 1) == 0) { sig >>= 1; ++tz; }
+        emin = std::min(emin, ex - 24 + tz);
+        amax = std::max(amax, std::fabs(v[i]));
+    }
+    int e = (emin == (1 << 30)) ? 0 : emin;
+    int8_t m[8];
+    for (int i = 0; i < 8; ++i) {
+        double q = std::ldexp((double)v[i], -e);
+        if (std::fabs(q) > 127.0 || q != std::floor(q)) return false;
+        m[i] = (int8_t)q;
+    }
+    (void)amax;
+    *lo = (uint32_t)(uint8_t)m[0] | ((uint32_t)(uint8_t)m[1] << 8) | ((uint32_t)(uint8_t)m[2] << 16) | ((uint32_t)(uint8_t)m[3] << 24);
+    *hi = (uint32_t)(uint8_t)m[4] | ((uint32_t)(uint8_t)m[5] << 8) | ((uint32_t)(uint8_t)m[6] << 16) | ((uint32_t)(uint8_t)m[7] << 24);
+    *scale = (float)std::ldexp(1.0, e);
+    return std::isfinite(*scale) && *scale != 0.f;
+}
+
+int check_gemv_args(const iqk_weights* w, const float* values, const int8_t* grid, const void* x, int x_dtype,
+                    int x_slots, const int32_t* ids, int64_t T, int k, const void* y, iqk::GemvLaunch* L) {
+    int rc = check_weights(w);
+    if (rc) return rc;
+    if (w->in != 512 && w->in != 2048 && w->in != 4096)
+        return fail(IQK_E_WIDTH, "decode matvec has no instance for input width %lld (instances: 512, 2048, 4096)",
+                    (long long)w->in);
+    if (T < 0 || k <= 0) return fail(IQK_E_ARG, "T must be >= 0 and k > 0");
+    if (T * k > 65535LL * 64) return fail(IQK_E_ARG, "T*k = %lld exceeds the decode limit", (long long)(T * k));
+    if (x_slots != 1 && x_slots != k) return fail(IQK_E_ARG, "x_slots must be 1 or k");
+    if (x_dtype != IQK_F32 && x_dtype != IQK_BF16) return fail(IQK_E_ARG, "x_dtype must be IQK_F32 or IQK_BF16");
+    if (T > 0 && (!x || !ids || !y)) return fail(IQK_E_ARG, "null x, ids or output");
+    L->fmt = w->fmt;
+    L->E = w->experts;
+    L->out = w->out;
+    L->n = w->in;
+    L->streams = (const uint8_t*)w->streams;
+    L->pl = iqk::planes(w->fmt, w->experts * w->out, w->in);
+    L->tab_lo = L->tab_hi = 0;
+    L->tab_scale = 1.f;
+    L->grid = grid;
+    if (w->fmt == IQK_IQ1_S_R4) {
+        if (!grid) return fail(IQK_E_ARG, "IQ1_S_R4 needs the device grid");
+    } else {
+        if (!values) return fail(IQK_E_ARG, "2-bit members need the host value table");
+        if (!table_to_int8(values, &L->tab_lo, &L->tab_hi, &L->tab_scale))
+            return fail(IQK_E_TABLE, "value table is not m_i * 2^e with |m_i| <= 127");
+    }
+    L->x = x;
+    L->x_dtype = x_dtype;
+    L->x_slots = x_slots;
+    L->ids = ids;
+    L->T = T;
+    L->k = k;
+    L->y = nullptr;
+    L->sink = nullptr;
+    return IQK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t iqk_row_bytes(int fmt, int64_t n) {
+    if (!known_fmt(fmt) || !iqk::shape_ok(fmt, n)) return 0;
+    return (size_t)iqk::row_bytes(fmt, n);
+}
+
+int iqk_plane_offsets(int fmt, int64_t rows, int64_t n, int64_t off[5], int64_t* total) {
+    int rc = check_fmt_shape(fmt, n);
+    if (rc) return rc;
+    if (rows < 0 || !off || !total) return fail(IQK_E_ARG, "bad rows or null output");
+    iqk::Planes p = iqk::planes(fmt, rows, n);
+    for (int i = 0; i < 5; ++i) off[i] = p.off[i];
+    *total = p.total;
+    return ok();
+}
+
+int iqk_pack_relayout(int fmt, const uint8_t* wire, size_t wire_bytes, int64_t rows, int64_t n, uint8_t* streams,
+                      size_t streams_bytes) {
+    int rc = check_relayout(fmt, wire, wire_bytes, rows, n, streams, streams_bytes);
+    if (rc) return rc;
+    Relayout L{fmt, rows, n, iqk::planes(fmt, rows, n)};
+    const int64_t units = fmt == IQK_IQ1_S_R4 ? rows / 4 : rows;
+    parallel_units(units, [&](int64_t u) { pack_unit(L, wire, streams, u); });
+    return ok();
+}
+
+int iqk_unpack_relayout(int fmt, const uint8_t* streams, size_t streams_bytes, int64_t rows, int64_t n, uint8_t* wire,
+                        size_t wire_bytes) {
+    int rc = check_relayout(fmt, streams, streams_bytes, rows, n, wire, wire_bytes);
+    if (rc) return rc;
+    Relayout L{fmt, rows, n, iqk::planes(fmt, rows, n)};
+    const int64_t units = fmt == IQK_IQ1_S_R4 ? rows / 4 : rows;
+    parallel_units(units, [&](int64_t u) { unpack_unit(L, streams, wire, u); });
+    return ok();
+}
+
+static int dequant_common(const iqk_weights* w, int64_t row0, int64_t nrows, const float* values, const int8_t* grid,
+                          int out_dtype, void* out, void* stream, bool floor_variant) {
+    int rc = check_weights(w);
+    if (rc) return rc;
+    const int64_t R = w->experts * w->out;
+    if (row0 < 0 || nrows < 0 || row0 + nrows > R) return fail(IQK_E_ARG, "row range outside the tensor");
+    if (out_dtype != IQK_F32 && out_dtype != IQK_F16 && out_dtype != IQK_BF16) return fail(IQK_E_ARG, "bad out_dtype");
+    if (nrows > 0 && !out) return fail(IQK_E_ARG, "null output");
+    iqk::DequantLaunch L;
+    L.fmt = w->fmt;
+    L.out_dtype = out_dtype;
+    L.R = R;
+    L.n = w->in;
+    L.row0 = row0;
+    L.nrows = nrows;
+    L.streams = (const uint8_t*)w->streams;
+    L.pl = iqk::planes(w->fmt, R, w->in);
+    for (int i = 0; i < 8; ++i) L.values[i] = 0.f;
+    L.grid = grid;
+    L.out = out;
+    if (!floor_variant) {
+        if (w->fmt == IQK_IQ1_S_R4) {
+            if (!grid) return fail(IQK_E_ARG, "IQ1_S_R4 needs the device grid");
+        } else {
+            if (!values) return fail(IQK_E_ARG, "2-bit members need the host value table");
+            for (int i = 0; i < 8; ++i) L.values[i] = values[i];
+        }
+    }
+    if (nrows == 0) return ok();
+    hipError_t e = iqk::launch_dequant(L, floor_variant, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, floor_variant ? "floor dequant launch" : "dequant launch");
+    return ok();
+}
+
+int iqk_dequant(const iqk_weights* w, int64_t row0, int64_t nrows, const float* values, const int8_t* grid,
+                int out_dtype, void* out, void* stream) {
+    return dequant_common(w, row0, nrows, values, grid, out_dtype, out, stream, false);
+}
+
+int iqk_floor_dequant(const iqk_weights* w, int64_t row0, int64_t nrows, int out_dtype, void* out, void* stream) {
+    return dequant_common(w, row0, nrows, nullptr, nullptr, out_dtype, out, stream, true);
+}
+
+int iqk_moe_gemv(const iqk_weights* w, const float* values, const int8_t* grid, const void* x, int x_dtype,
+                 int x_slots, const int32_t* ids, int64_t T, int k, float* y, void* stream) {
+    iqk::GemvLaunch L;
+    int rc = check_gemv_args(w, values, grid, x, x_dtype, x_slots, ids, T, k, y, &L);
+    if (rc) return rc;
+    L.y = y;
+    if (T == 0) return ok();
+    hipError_t e = iqk::launch_gemv(L, false, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "decode matvec launch");
+    return ok();
+}
+
+int iqk_floor_gemv(const iqk_weights* w, const float* values, const int8_t* grid, const void* x, int x_dtype,
+                   int x_slots, const int32_t* ids, int64_t T, int k, uint32_t* sink, void* stream) {
+    iqk::GemvLaunch L;
+    int rc = check_gemv_args(w, values, grid, x, x_dtype, x_slots, ids, T, k, sink, &L);
+    if (rc) return rc;
+    L.sink = sink;
+    if (T == 0) return ok();
+    hipError_t e = iqk::launch_gemv(L, true, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "floor matvec launch");
+    return ok();
+}
+
+int iqk_route(const int32_t* ids, int64_t P, int64_t E, int sorted, int32_t* counts, int32_t* offsets, int32_t* perm,
+              void* stream) {
+    if (P < 0 || P > (1LL << 24)) return fail(IQK_E_ARG, "pair count %lld outside [0, 2^24]", (long long)P);
+    if (E <= 0 || E > 16384) return fail(IQK_E_ARG, "expert count %lld outside [1, 16384]", (long long)E);
+    if (sorted != 0 && sorted != 1) return fail(IQK_E_ARG, "sorted must be 0 or 1");
+    if (!counts || !offsets || (P > 0 && (!ids || !perm))) return fail(IQK_E_ARG, "null pointer");
+    iqk::RouteLaunch L{ids, P, E, sorted, counts, offsets, perm};
+    hipError_t e = iqk::launch_route(L, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "route launch");
+    return ok();
+}
+
+int iqk_grouped_gemm(const void* W_bf16, int64_t E, int64_t out, int64_t in, const void* x_bf16, int x_slots,
+                     int64_t T, int k, const int32_t* offsets, const int32_t* perm, float* y, void* stream) {
+    if (E <= 0 || out <= 0 || in <= 0 || T < 0 || k <= 0) return fail(IQK_E_ARG, "bad sizes");
+    if (in % 64) return fail(IQK_E_SHAPE, "grouped GEMM needs in %% 64 == 0");
+    if (out % 16) return fail(IQK_E_SHAPE, "grouped GEMM needs out %% 16 == 0");
+    if (x_slots != 1 && x_slots != k) return fail(IQK_E_ARG, "x_slots must be 1 or k");
+    if (T * k > (1LL << 24)) return fail(IQK_E_ARG, "too many pairs");
+    if (!W_bf16 || !offsets || (T > 0 && (!x_bf16 || !perm || !y))) return fail(IQK_E_ARG, "null pointer");
+    if (T == 0) return ok();
+    iqk::GemmLaunch L{W_bf16, E, out, in, x_bf16, x_slots, T, k, offsets, perm, y};
+    hipError_t e = iqk::launch_grouped_gemm(L, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "grouped GEMM launch");
+    return ok();
+}
+
+static size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+int iqk_moe_prefill_workspace(const iqk_weights* w, int64_t T, int k, size_t* bytes) {
+    if (!w || !bytes) return fail(IQK_E_ARG, "null pointer");
+    int rc = check_fmt_shape(w->fmt, w->in);
+    if (rc) return rc;
+    if (w->experts <= 0 || w->out <= 0 || T < 0 || k <= 0) return fail(IQK_E_ARG, "bad sizes");
+    const int64_t P = T * k;
+    *bytes = round256((size_t)(w->experts * w->out * w->in) * 2) + round256((size_t)w->experts * 4) +
+             round256((size_t)(w->experts + 1) * 4) + round256((size_t)std::max<int64_t>(P, 1) * 4);
+    return ok();
+}
+
+int iqk_moe_prefill(const iqk_weights* w, const float* values, const int8_t* grid, const void* x_bf16, int x_slots,
+                    const int32_t* ids, int64_t T, int k, int sorted, void* workspace, size_t ws_bytes, float* y,
+                    void* stream) {
+    int rc = check_weights(w);
+    if (rc) return rc;
+    if (T < 0 || k <= 0) return fail(IQK_E_ARG, "T must be >= 0 and k > 0");
+    if (T * k > (1LL << 24)) return fail(IQK_E_ARG, "too many pairs");
+    if (x_slots != 1 && x_slots != k) return fail(IQK_E_ARG, "x_slots must be 1 or k");
+    if (sorted != 0 && sorted != 1) return fail(IQK_E_ARG, "sorted must be 0 or 1");
+    if (w->out % 16) return fail(IQK_E_SHAPE, "prefill needs out %% 16 == 0");
+    if (w->in % 64) return fail(IQK_E_SHAPE, "prefill needs in %% 64 == 0");
+    if (w->experts > 16384) return fail(IQK_E_ARG, "prefill routing supports at most 16384 experts");
+    if (w->fmt == IQK_IQ1_S_R4 ? !grid : !values) return fail(IQK_E_ARG, "missing value table or grid");
+    size_t need = 0;
+    rc = iqk_moe_prefill_workspace(w, T, k, &need);
+    if (rc) return rc;
+    if (!workspace || ws_bytes < need) return fail(IQK_E_SIZE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+    if (T > 0 && (!x_bf16 || !ids || !y)) return fail(IQK_E_ARG, "null x, ids or output");
+    if (T == 0) return ok();
+    const int64_t E = w->experts, P = T * k;
+    uint8_t* ws = (uint8_t*)workspace;
+    void* dense = ws;
+    ws += round256((size_t)(E * w->out * w->in) * 2);
+    int32_t* counts = (int32_t*)ws;
+    ws += round256((size_t)E * 4);
+    int32_t* offsets = (int32_t*)ws;
+    ws += round256((size_t)(E + 1) * 4);
+    int32_t* perm = (int32_t*)ws;
+    hipStream_t s = (hipStream_t)stream;
+    iqk::RouteLaunch RL{ids, P, E, sorted, counts, offsets, perm};
+    hipError_t e = iqk::launch_route(RL, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill route launch");
+    rc = iqk_dequant(w, 0, E * w->out, values, grid, IQK_BF16, dense, stream);
+    if (rc) return rc;
+    iqk::GemmLaunch GL{dense, E, w->out, w->in, x_bf16, x_slots, T, k, offsets, perm, y};
+    e = iqk::launch_grouped_gemm(GL, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill grouped GEMM launch");
+    return ok();
+}
+
+int iqk_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, void* stream) {
+    if (!buf || !sink || bytes == 0 || bytes % 16 || sink_words == 0) return fail(IQK_E_ARG, "bad stream-read arguments");
+    hipError_t e = iqk::launch_stream_read(buf, bytes, sink, sink_words, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "stream read launch");
+    return ok();
+}
+
+const char* iqk_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

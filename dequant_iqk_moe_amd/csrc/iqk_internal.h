@@ -1,0 +1,109 @@
+// iqk_internal.h -- shared between the host entry points and the HIP kernels
+// of the IQ_K routed-expert library.  Nothing here is part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/iqk.h"
+
+namespace iqk {
+
+// Plane byte offsets of an R-row canonical stream tensor (see iqk.h).
+struct Planes {
+    int64_t off[5];
+    int64_t total;
+};
+
+inline bool shape_ok(int fmt, int64_t n) {
+    if (n <= 0) return false;
+    if (fmt == IQK_IQ2_KS || fmt == IQK_IQ2_K) return n % 256 == 0;
+    if (fmt == IQK_IQ1_S_R4) return n % 32 == 0;
+    return false;
+}
+
+inline int64_t row_bytes(int fmt, int64_t n) {
+    if (fmt == IQK_IQ2_KS) return 2 + 70 * n / 256;
+    if (fmt == IQK_IQ2_K) return 76 * n / 256;
+    return 2 + 6 * n / 32;
+}
+
+inline Planes planes(int fmt, int64_t R, int64_t n) {
+    Planes p;
+    for (int i = 0; i < 5; ++i) p.off[i] = -1;
+    if (fmt == IQK_IQ2_KS) {
+        p.off[0] = 0;                       // qs
+        p.off[1] = p.off[0] + R * n / 4;    // scl
+        p.off[2] = p.off[1] + R * n / 64;   // sch
+        p.off[3] = p.off[2] + R * n / 256;  // sex
+        p.off[4] = p.off[3] + R * n / 256;  // dv
+    } else if (fmt == IQK_IQ2_K) {
+        p.off[0] = 0;                       // qs
+        p.off[1] = p.off[0] + R * n / 4;    // scl
+        p.off[2] = p.off[1] + R * n / 32;   // sex
+        p.off[3] = p.off[2] + R * n / 128;  // dv
+    } else {
+        p.off[0] = 0;                       // qs
+        p.off[1] = p.off[0] + R * n / 8;    // qh
+        p.off[2] = p.off[1] + R * (n / 32) * 2;  // dv
+    }
+    p.total = R * row_bytes(fmt, n);
+    return p;
+}
+
+// Dequantization / producer launch description.
+struct DequantLaunch {
+    int fmt;
+    int out_dtype;
+    int64_t R, n, row0, nrows;
+    const uint8_t* streams;
+    Planes pl;
+    float values[8];
+    const int8_t* grid;
+    void* out;
+};
+
+// Decode matvec launch description.
+struct GemvLaunch {
+    int fmt;
+    int64_t E, out, n;
+    const uint8_t* streams;
+    Planes pl;
+    uint32_t tab_lo, tab_hi;  // int8 table m_0..m_3 and m_4..m_7
+    float tab_scale;          // 2^e with values[i] = m_i * 2^e
+    const int8_t* grid;
+    const void* x;
+    int x_dtype, x_slots;
+    const int32_t* ids;
+    int64_t T;
+    int k;
+    float* y;
+    uint32_t* sink;  // floor variant output (y unused)
+};
+
+struct RouteLaunch {
+    const int32_t* ids;
+    int64_t P, E;
+    int sorted;
+    int32_t *counts, *offsets, *perm;
+};
+
+struct GemmLaunch {
+    const void* W;
+    int64_t E, out, n;
+    const void* x;
+    int x_slots;
+    int64_t T;
+    int k;
+    const int32_t *offsets, *perm;
+    float* y;
+};
+
+hipError_t launch_dequant(const DequantLaunch& a, bool floor_variant, hipStream_t s);
+hipError_t launch_gemv(const GemvLaunch& a, bool floor_variant, hipStream_t s);
+hipError_t launch_route(const RouteLaunch& a, hipStream_t s);
+hipError_t launch_grouped_gemm(const GemmLaunch& a, hipStream_t s);
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, hipStream_t s);
+
+}  // namespace iqk

@@ -1,0 +1,211 @@
+/*
+ * iqk.h -- C ABI of the MI355X (gfx950) IQ_K routed-expert library.
+ *
+ * The operations follow the "mlx-iqk" package description (IQ_K relayout
+ * routed-expert kernels):
+ *   - "Format" section: the per-row streams of IQ2_KS (qs, scl, sch, sex,
+ *     dv), IQ2_K (qs, scl, sex, dv) and IQ1_S_R4 (qs, qh, dv); the two float32
+ *     reconstruction chains; the row budgets 2 + 70n/256, 76n/256 and
+ *     2 + 6n/32 bytes; the IQ1_S_R4 wire in whole four-row groups;
+ *   - introduction: the build-time relayout that makes values consumed
+ *     along k contiguous without changing a value or a byte budget;
+ *   - "Surface" section: the switch-linear call y = proj(x, indices): few
+ *     token-expert pairs run a fused decode matvec, many pairs run a
+ *     one-pass dequantization of the stacked experts followed by a grouped
+ *     GEMM that reads each expert once when pairs are sorted by expert; the
+ *     decode kernel exists only for instantiated input widths and any other
+ *     width is refused.
+ *
+ * Conventions for every call:
+ *   - Plain pointers and sizes.  "host" pointers are CPU memory, "device"
+ *     pointers are HIP device memory of the current device.  The caller owns
+ *     every buffer; the library allocates nothing and keeps no state except a
+ *     per-thread error message.
+ *   - Every argument is validated before any HIP call.  A failed check
+ *     returns a negative iqk_status, touches no buffer, enqueues nothing and
+ *     sets iqk_last_error().
+ *   - Device calls enqueue on `stream` (a hipStream_t; NULL = the null
+ *     stream) and return without synchronizing.  Launch failures return
+ *     IQK_E_HIP with the HIP error text in iqk_last_error().
+ *   - Calls that overlap on one stream are ordered; calls on different
+ *     streams that write the same output race.
+ *
+ * Stream tensors ("served relayout", canonical layout of this library).  A
+ * weight descriptor covers E experts of [out, in] stacked to R = E*out rows.
+ * Each stream is a plane over all R rows, row-major, k-contiguous, with no
+ * padding; planes follow the order of the stream tables; bits are LSB-first
+ * within bytes (equivalently, element i of a plane of w-bit elements sits at
+ * bits [w*i mod 32, +w) of little-endian uint32 word w*i/32):
+ *   IQ2_KS  (in % 256 == 0): qs R*in/4 (2-bit code per weight) | scl R*in/64
+ *           (4-bit low part of the scale index per 32 weights) | sch R*in/256
+ *           (high bit per 32 weights) | sex R*in/256 (alphabet bit per 32
+ *           weights) | dv R*2 (fp16 row scale).
+ *           scale_index = (scl | sch << 4) - 16, in [-16, 15].
+ *   IQ2_K   (in % 256 == 0): qs R*in/4 | scl R*in/32 (4-bit per 16 weights,
+ *           scale_index = scl - 8) | sex R*in/128 (bit per 16 weights) |
+ *           dv R*(in/256)*2 (fp16 per 256 weights).
+ *   IQ1_S_R4 (in % 32 == 0): qs R*in/8 (low 8 bits of the 11-bit grid index
+ *           per 8 weights; block b of 32 weights is uint32 word b) |
+ *           qh R*(in/32)*2 (uint16 per 32 weights: bits 3j..3j+2 = index high
+ *           bits of group j, bits 12..14 = ls, bit 15 = shift sign, set means
+ *           -0.125) | dv R*2 (fp16 row scale).
+ * Reconstruction (float32, every step rounded, in this order):
+ *   2-bit:   w = (float(dv) * float(scale_index)) * values[4*alphabet + code]
+ *   IQ1_S_R4: w = (float(dv) * float(2*ls + 1)) * (float(grid[idx][k%8]) + shift)
+ *
+ * Wire tensors (ik block structs, per "Format": the same byte budgets).
+ * The bit positions inside the blocks are this library's stand-in reading:
+ *   IQ2_KS per row: fp16 d, then in/256 blocks of 70 B {uint16 extra (bit s =
+ *     alphabet of sub-block s, bit 8+s = scale high bit), uint8 scales[4]
+ *     (low nibble sub-block 2i, high nibble 2i+1), uint8 qs[64]}.
+ *   IQ2_K per row: in/256 blocks of 76 B {fp16 d, uint16 extra (bit s =
+ *     alphabet of sub-block s), uint8 scales[8], uint8 qs[64]}.
+ *   qs of both: weight 128h + 32p + l of a block -> byte 32h + l, bits 2p.
+ *   IQ1_S_R4 per four-row group: fp16 d[4], then in/32 blocks of 24 B
+ *     {uint8 qs[16] (byte 4j + r = group j of row r), uint16 qh[4]}.
+ */
+#ifndef IQK_H
+#define IQK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { IQK_IQ2_KS = 1, IQK_IQ2_K = 2, IQK_IQ1_S_R4 = 3 } iqk_format;
+typedef enum { IQK_F32 = 0, IQK_F16 = 1, IQK_BF16 = 2 } iqk_dtype;
+typedef enum {
+    IQK_OK = 0,
+    IQK_E_ARG = -1,     /* null pointer, negative size, bad enum, bad count */
+    IQK_E_FORMAT = -2,  /* unknown format */
+    IQK_E_SHAPE = -3,   /* in % 256 (2-bit members) or in % 32 (IQ1_S_R4) != 0 */
+    IQK_E_WIDTH = -4,   /* decode matvec: no instance for this input width */
+    IQK_E_ROWS4 = -5,   /* IQ1_S_R4 wire: rows not a multiple of four */
+    IQK_E_SIZE = -6,    /* a byte count does not match the layout */
+    IQK_E_TABLE = -7,   /* decode matvec: value table not of the form m_i * 2^e, |m_i| <= 127 */
+    IQK_E_HIP = -8      /* HIP runtime error */
+} iqk_status;
+
+/* Expert-stacked weights: `experts` tensors of [out, in], R = experts*out rows
+ * in the canonical stream layout above.  `streams` is a device pointer of
+ * exactly `streams_bytes` = R * iqk_row_bytes(fmt, in) bytes. */
+typedef struct iqk_weights {
+    int32_t fmt;
+    int64_t experts, out, in;
+    const void* streams;
+    size_t streams_bytes;
+} iqk_weights;
+
+/* Bytes of one row of `n` weights ("Format": row budgets); 0 if the format is
+ * unknown or n violates its shape rule. */
+size_t iqk_row_bytes(int fmt, int64_t n);
+
+/* Byte offsets of the planes of an R-row stream tensor (unused entries = -1):
+ * IQ2_KS {qs, scl, sch, sex, dv}; IQ2_K {qs, scl, sex, dv, -1};
+ * IQ1_S_R4 {qs, qh, dv, -1, -1}.  *total = R * iqk_row_bytes(fmt, n). */
+int iqk_plane_offsets(int fmt, int64_t rows, int64_t n, int64_t off[5], int64_t* total);
+
+/* Relayout ("Format" / introduction): wire -> canonical streams, a pure bit
+ * permutation with equal byte counts.  Host memory, synchronous.  Both
+ * buffers must hold exactly rows * iqk_row_bytes(fmt, n) bytes; IQ1_S_R4
+ * needs rows % 4 == 0 (IQK_E_ROWS4).  `wire` and `streams` must not overlap. */
+int iqk_pack_relayout(int fmt, const uint8_t* wire, size_t wire_bytes, int64_t rows, int64_t n,
+                      uint8_t* streams, size_t streams_bytes);
+/* The inverse permutation: canonical streams -> wire. */
+int iqk_unpack_relayout(int fmt, const uint8_t* streams, size_t streams_bytes, int64_t rows, int64_t n,
+                        uint8_t* wire, size_t wire_bytes);
+
+/* Dequantization ("Format" reconstruction; the prefill weight producer of
+ * "Surface"): rows [row0, row0 + nrows) of the stacked tensor -> `out`
+ * [nrows, in] (device, dense, row-major) in `out_dtype`.  float32 results
+ * are bit-exact with the float32 chain; f16 / bf16 results are one
+ * round-to-nearest-even cast of it (NaN results are quiet NaNs of
+ * unspecified payload).
+ * `values`: host float[8] for the 2-bit members (any float32 values),
+ * ignored for IQ1_S_R4.  `grid`: device int8[2048*8] (row idx = 8 grid
+ * values) for IQ1_S_R4, ignored otherwise. */
+int iqk_dequant(const iqk_weights* w, int64_t row0, int64_t nrows, const float* values,
+                const int8_t* grid, int out_dtype, void* out, void* stream);
+
+/* Fused decode matvec ("Surface": few token-expert pairs).
+ * y[t, j, o] = sum_k W_{ids[t,j]}[o, k] * x[t, s, k] with s = 0 if
+ * x_slots == 1 (shared input, gate/up) or s = j if x_slots == k (per-pair
+ * input, down).  x: device [T, x_slots, in] of x_dtype IQK_F32 or IQK_BF16.
+ * ids: device int32 [T, k]; an id outside [0, experts) gives a NaN output
+ * row.  y: device float32 [T, k, out].
+ * Widths: in must be 512, 2048 or 4096 (IQK_E_WIDTH otherwise): a kernel
+ * instance makes exactly one pass over k.  The values table (host float[8])
+ * must be m_i * 2^e with integer |m_i| <= 127 for one common e (integer
+ * tables qualify), else IQK_E_TABLE.  Accuracy: the activation is held per
+ * 64-value block as 15-bit fixed point (relative error about 2^-14 of the
+ * block maximum); weights and sums are exact integers up to one float32
+ * rounding per row; ||y - y_exact|| / ||y_exact|| <= 1e-3.
+ * Limits: T * k <= 65535 * 64. */
+int iqk_moe_gemv(const iqk_weights* w, const float* values, const int8_t* grid,
+                 const void* x, int x_dtype, int x_slots, const int32_t* ids,
+                 int64_t T, int k, float* y, void* stream);
+
+/* Routing gather ("Surface": sorting pairs by expert so that each expert's
+ * weights are read once).  ids: device int32 [P] (P = T*k pair indices
+ * t*k + j).  Writes device int32 counts[E], offsets[E+1] (exclusive prefix
+ * sum) and perm[P]: pair indices grouped by increasing expert, increasing
+ * pair index inside an expert (a stable sort); pairs with an id outside
+ * [0, E) are dropped and the remaining perm entries are set to -1.
+ * `sorted` = 1 states that ids are already non-decreasing (the caller's
+ * sort flag); the result is the same either way.  P <= 2^24, E <= 16384. */
+int iqk_route(const int32_t* ids, int64_t P, int64_t E, int sorted,
+              int32_t* counts, int32_t* offsets, int32_t* perm, void* stream);
+
+/* Grouped GEMM over expert-stacked dense bf16 weights (MLX's gather_mm in
+ * "Surface"): for every routed pair p = t*k + j with expert e,
+ * y[p, :] = W[e] @ x[t, s, :] (s as in iqk_moe_gemv), bf16 inputs, float32
+ * accumulation on MFMA.  W: device bf16 [E, out, in]; x: device bf16
+ * [T, x_slots, in]; offsets / perm from iqk_route; y: device float32
+ * [T, k, out]; rows of dropped pairs are left untouched.  in % 64 == 0,
+ * out % 16 == 0, E <= 16384. */
+int iqk_grouped_gemm(const void* W_bf16, int64_t E, int64_t out, int64_t in,
+                     const void* x_bf16, int x_slots, int64_t T, int k,
+                     const int32_t* offsets, const int32_t* perm, float* y, void* stream);
+
+/* Workspace of iqk_moe_prefill: the dense bf16 copy of all experts plus the
+ * routing arrays, each rounded up to 256 bytes. */
+int iqk_moe_prefill_workspace(const iqk_weights* w, int64_t T, int k, size_t* bytes);
+
+/* Prefill ("Surface": many pairs): iqk_route, then iqk_dequant of all
+ * experts to bf16 in the workspace ("dequantizes the stacked experts in one
+ * kernel pass"), then iqk_grouped_gemm.  x: device bf16 [T, x_slots, in];
+ * y: device float32 [T, k, out]; invalid ids leave their rows untouched.
+ * Accuracy against the float32-weight product: ||y - y_exact|| /
+ * ||y_exact|| <= 2e-2 (bf16 weights). */
+int iqk_moe_prefill(const iqk_weights* w, const float* values, const int8_t* grid,
+                    const void* x_bf16, int x_slots, const int32_t* ids, int64_t T, int k,
+                    int sorted, void* workspace, size_t ws_bytes, float* y, void* stream);
+
+/* Measurement kernels for the deleted-decode address floor ("Pricing"
+ * section: identical loads, decode removed, an integer accumulator reaching
+ * the output).  iqk_floor_gemv issues the same loads as iqk_moe_gemv for the
+ * same arguments (including the activation conversion), replaces the weight
+ * decode with an integer XOR/add accumulator and writes one uint32 per
+ * output element to `sink` (device [T, k, out]).  iqk_floor_dequant issues
+ * the same loads and the same stores as iqk_dequant into `out` (device,
+ * [nrows, in] of out_dtype) with the loaded words in place of the decoded
+ * weights.  iqk_stream_read XOR-reduces `bytes` (a multiple of 16) of
+ * device memory as a plain HBM streaming read and stores partial results
+ * to sink[sink_words]. */
+int iqk_floor_gemv(const iqk_weights* w, const float* values, const int8_t* grid,
+                   const void* x, int x_dtype, int x_slots, const int32_t* ids,
+                   int64_t T, int k, uint32_t* sink, void* stream);
+int iqk_floor_dequant(const iqk_weights* w, int64_t row0, int64_t nrows, int out_dtype,
+                      void* out, void* stream);
+int iqk_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* iqk_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IQK_H */

@@ -20,3 +20,14 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "slow" in it.keywords:
             it.add_marker(skip)
+
+
+def _ensure_built():
+    """Build the HIP library in-tree only when nothing is built yet."""
+    lib = os.path.join(ROOT, "dequant_iqk_moe_amd", "libiqk.so")
+    if not os.path.exists(lib):
+        from dequant_iqk_moe_amd import build as _b
+        _b.build()
+
+
+_ensure_built()
