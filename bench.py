@@ -185,6 +185,19 @@ def main():
 
     ms_floor, _ = _timed_graph(torch, gu_floor, S, reps, warm)
 
+    # plain streaming read of the same byte count (floor-rate reference)
+    nb = int(gu_bytes) // 16 * 16
+    slots = 64
+    sbuf = torch.empty(nb * slots, dtype=torch.uint8, device="cuda")
+    sbuf.fill_(1)
+    ssink = torch.zeros(1 << 14, dtype=torch.int32, device="cuda")
+
+    def sread(i):
+        q.stream_read(sbuf[(i % slots) * nb:(i % slots + 1) * nb], ssink)
+
+    ms_stream, _ = _timed_graph(torch, sread, S, reps, warm)
+    del sbuf
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle as orc
@@ -221,6 +234,8 @@ def main():
                      "bytes_per_launch": int(gu_bytes), "us_per_launch": round(ms_gu * 1e3, 3)},
         "ratio_to_own_floor": round(ms_gu / ms_floor, 4),
         "floor_us_per_launch": round(ms_floor * 1e3, 3),
+        "stream_read_us_same_bytes": round(ms_stream * 1e3, 3),
+        "floor_rate_vs_stream": round(ms_stream / ms_floor, 4),
         "validation_worst_err": worst,
         "setup_s": round(setup_s, 1),
         "cpu_baseline": cpu,

@@ -11,7 +11,7 @@
 //
 // gfx950 design.  The matvec is bound by HBM bytes, but at 8 TB/s the
 // vector ALUs have only ~1.3-1.5 lane-instructions per weight, so the decode
-// must be integer and 4-wide:
+// is integer and 4-wide:
 //   * each lane owns 64 consecutive k of a row (one 16-byte load of the code
 //     plane); a wave covers 4096 k per load instruction (1 row at in=4096,
 //     2 rows at 2048, 8 rows at 512), every load coalesced along k;
@@ -29,15 +29,25 @@
 //     shift is applied through the block sum of x;
 //   * per-lane partials of 4 rows are reduced with v_permlane32_swap,
 //     v_permlane16_swap and DPP (10 instructions per 4 rows).
-// Rows are wave-contiguous so the small per-row planes share cache lines
-// inside one workgroup.  Result: y[t, j, o] in float32.
+// Latency: a decode launch is a few microseconds long.  The activation is
+// read and converted first (row loads issued before it would queue ahead of
+// it), the workgroup barrier waits only for LDS traffic, every wave then
+// requests its first two row groups at once and each later group two groups
+// ahead.  One large workgroup per CU (up to 16 waves)
+// amortizes the activation conversion over ~100 rows.  Rows of a workgroup
+// are contiguous, so the small per-row planes share cache lines.
 #include "iqk_internal.h"
 
 namespace iqk {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+#ifndef IQK_GEMV_TARGET_BLOCKS
+#define IQK_GEMV_TARGET_BLOCKS 256  // workgroups per launch (one per CU)
+#endif
+#ifndef IQK_GEMV_MIN_GROUPS
+#define IQK_GEMV_MIN_GROUPS 2       // reduction groups per wave when the block has >= 8
+#endif
+constexpr int kMaxWaves = 16;
 
 struct GemvParams {
     const uint8_t* S;
@@ -51,9 +61,8 @@ struct GemvParams {
     const int32_t* ids;
     float* y;
     uint32_t* sink;
-    int32_t nrb;      // row blocks per pair
-    int32_t groups;   // reduction groups per wave
-    int32_t rows_wg;  // rows per workgroup
+    int32_t nrb;     // row blocks per pair
+    int32_t groups;  // reduction groups per wave
 };
 
 template <int N>
@@ -66,6 +75,12 @@ struct Geo {
 
 __device__ __forceinline__ float half_to_float(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// Workgroup barrier for LDS only: global loads issued before it stay in
+// flight (a full __syncthreads would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) { return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false); }
@@ -147,22 +162,22 @@ struct XLds {
     int32_t bsum[N / 32];
 };
 
-// Convert 16 activation values (one 16-block of a chunk) per thread.
+// Convert one 16-value block of the activation (block index b; the four
+// blocks of a 64-value chunk sit in four consecutive lanes).
 template <int FMT, int N, int XDT>
-__device__ __forceinline__ void prep_x(const void* xrow, XLds<N>& L, int tid) {
-    if (tid >= N / 16) return;
+__device__ __forceinline__ void prep_block(const void* xrow, XLds<N>& L, int b) {
     float v[16];
     if constexpr (XDT == IQK_BF16) {
-        const uint4* src = (const uint4*)xrow + 2 * tid;
-        const uint4 a = src[0], b = src[1];
-        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        const uint4* src = (const uint4*)xrow + 2 * b;
+        const uint4 a = src[0], c = src[1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             v[2 * i] = __uint_as_float(w[i] << 16);
             v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
         }
     } else {
-        const float4* src = (const float4*)xrow + 4 * tid;
+        const float4* src = (const float4*)xrow + 4 * b;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float4 f = src[i];
@@ -175,7 +190,6 @@ __device__ __forceinline__ void prep_x(const void* xrow, XLds<N>& L, int tid) {
     uint32_t amax = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax = max(amax, __float_as_uint(v[i]) & 0x7FFFFFFFu);
-    // chunk = 4 consecutive threads
     amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
     amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
     int emax = (int)(amax >> 23) - 127;
@@ -200,81 +214,127 @@ __device__ __forceinline__ void prep_x(const void* xrow, XLds<N>& L, int tid) {
         wl[j] = (uint32_t)(lo[i0] & 0xFF) | ((uint32_t)(lo[i0 + st] & 0xFF) << 8) |
                 ((uint32_t)(lo[i0 + 2 * st] & 0xFF) << 16) | ((uint32_t)(lo[i0 + 3 * st] & 0xFF) << 24);
     }
-    *(uint4*)&L.hi[4 * tid] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-    *(uint4*)&L.lo[4 * tid] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
-    if ((tid & 3) == 0) L.scale[tid >> 2] = __builtin_ldexpf(1.0f, emax - 13);
+    *(uint4*)&L.hi[4 * b] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+    *(uint4*)&L.lo[4 * b] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+    if ((b & 3) == 0) L.scale[b >> 2] = __builtin_ldexpf(1.0f, emax - 13);
     if constexpr (FMT == IQK_IQ1_S_R4) {
         int sum = 0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sum += q[i];
         sum += __shfl_xor(sum, 1);
-        if ((tid & 1) == 0) L.bsum[tid >> 1] = sum;
+        if ((b & 1) == 0) L.bsum[b >> 1] = sum;
     }
 }
 
-template <int FMT>
+// Raw stream words of the 64 weights one lane owns in one row.
 struct RowData {
-    uint4 q;       // codes / low index bytes (IQ1_S_R4 uses q.x, q.y)
+    uint4 q;  // codes (IQ1_S_R4: q.x, q.y = low index bytes of 8 groups)
     uint32_t a, b, c, d;
 };
 
+// Byte strides of the planes per row.
 template <int FMT, int N>
-__device__ __forceinline__ RowData<FMT> load_row(const GemvParams& p, int64_t grow, int c) {
-    RowData<FMT> r;
+struct Strides {
+    static constexpr int QS = FMT == IQK_IQ1_S_R4 ? N / 8 : N / 4;
+    static constexpr int P1 = FMT == IQK_IQ2_K ? N / 32 : (FMT == IQK_IQ2_KS ? N / 64 : N / 16);
+    static constexpr int P2 = FMT == IQK_IQ2_K ? N / 128 : (FMT == IQK_IQ2_KS ? N / 256 : 2);
+    static constexpr int P3 = FMT == IQK_IQ2_K ? N / 128 : (FMT == IQK_IQ2_KS ? N / 256 : 0);
+    static constexpr int P4 = FMT == IQK_IQ2_KS ? 2 : 0;
+};
+
+// Load the words of one lane for the row `grow0 + dl` (grow0 uniform, dl the
+// lane's non-negative row offset inside the iteration).  Plane base pointers
+// are uniform and lane offsets unsigned 32-bit, so every load is the
+// scalar-base + vector-offset form.
+template <int FMT, int N>
+__device__ __forceinline__ RowData load_row(const GemvParams& p, int64_t grow0, uint32_t dl, uint32_t c) {
+    using St = Strides<FMT, N>;
+    RowData r;
     const uint8_t* S = p.S;
     if constexpr (FMT == IQK_IQ2_K) {
-        r.q = *(const uint4*)(S + p.off0 + grow * (N / 4) + 16 * c);
-        r.a = *(const uint16_t*)(S + p.off1 + grow * (N / 32) + 2 * c);
-        r.b = S[p.off2 + grow * (N / 128) + (c >> 1)];
+        const uint8_t* b0 = S + p.off0 + grow0 * St::QS;
+        const uint8_t* b1 = S + p.off1 + grow0 * St::P1;
+        const uint8_t* b2 = S + p.off2 + grow0 * St::P2;
+        const uint8_t* b3 = S + p.off3 + grow0 * St::P3;
+        r.q = *(const uint4*)(b0 + (dl * (uint32_t)St::QS + 16u * c));
+        r.a = *(const uint16_t*)(b1 + (dl * (uint32_t)St::P1 + 2u * c));
+        r.b = b2[dl * (uint32_t)St::P2 + (c >> 1)];
         r.c = 0;
-        r.d = *(const uint16_t*)(S + p.off3 + grow * (N / 128) + 2 * (c >> 2));
+        r.d = *(const uint16_t*)(b3 + (dl * (uint32_t)St::P3 + 2u * (c >> 2)));
     } else if constexpr (FMT == IQK_IQ2_KS) {
-        r.q = *(const uint4*)(S + p.off0 + grow * (N / 4) + 16 * c);
-        r.a = S[p.off1 + grow * (N / 64) + c];
-        r.b = S[p.off2 + grow * (N / 256) + (c >> 2)];
-        r.c = S[p.off3 + grow * (N / 256) + (c >> 2)];
-        r.d = *(const uint16_t*)(S + p.off4 + 2 * grow);
+        const uint8_t* b0 = S + p.off0 + grow0 * St::QS;
+        const uint8_t* b1 = S + p.off1 + grow0 * St::P1;
+        const uint8_t* b2 = S + p.off2 + grow0 * St::P2;
+        const uint8_t* b3 = S + p.off3 + grow0 * St::P3;
+        const uint8_t* b4 = S + p.off4 + grow0 * 2;
+        r.q = *(const uint4*)(b0 + (dl * (uint32_t)St::QS + 16u * c));
+        r.a = b1[dl * (uint32_t)St::P1 + c];
+        r.b = b2[dl * (uint32_t)St::P2 + (c >> 2)];
+        r.c = b3[dl * (uint32_t)St::P3 + (c >> 2)];
+        r.d = *(const uint16_t*)(b4 + 2u * dl);
     } else {
-        const uint2 qq = *(const uint2*)(S + p.off0 + grow * (N / 8) + 8 * c);
+        const uint8_t* b0 = S + p.off0 + grow0 * St::QS;
+        const uint8_t* b1 = S + p.off1 + grow0 * St::P1;
+        const uint8_t* b2 = S + p.off2 + grow0 * 2;
+        const uint2 qq = *(const uint2*)(b0 + (dl * (uint32_t)St::QS + 8u * c));
         r.q = make_uint4(qq.x, qq.y, 0, 0);
-        r.a = *(const uint32_t*)(S + p.off1 + grow * (N / 16) + 4 * c);
+        r.a = *(const uint32_t*)(b1 + (dl * (uint32_t)St::P1 + 4u * c));
         r.b = 0;
         r.c = 0;
-        r.d = *(const uint16_t*)(S + p.off2 + 2 * grow);
+        r.d = *(const uint16_t*)(b2 + 2u * dl);
     }
     return r;
 }
 
-// Dot of one lane's 64 weights with its 64 activations, in units of
-// (fixed-point x) * (int8 table): returns the float partial before the
-// per-lane scale (d * x-chunk scale * table scale) for the 2-bit members,
-// and including d-independent factors for IQ1_S_R4.
+// d = dot4(a, b) with the accumulator starting at zero (VOP3P form with an
+// inline zero instead of a v_mov plus v_dot4c).
+__device__ __forceinline__ int dot4_first(uint32_t a, uint32_t b) {
+    int d;
+    asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+}
+
+// (a & b) | c in one v_bitop3_b32.  The truth table is indexed by
+// (a << 2) | (b << 1) | c, so (a & b) | c is 0xEA.  On gfx950 the bitop3
+// issues at the rate of the two-operand bitwise ops, about twice the rate of
+// v_and_or_b32.
+__device__ __forceinline__ uint32_t and_or_fast(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t d;
+    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0xea" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+
+// 16 weights of one code word against 4 activation words.
+template <bool FIRST>
 __device__ __forceinline__ int dot16(uint32_t qw, uint32_t m, uint32_t tlo, uint32_t thi, const uint32_t* x4, int acc) {
     const uint32_t M = 0x03030303u;
-    const uint32_t w0 = __builtin_amdgcn_perm(thi, tlo, (qw & M) | m);
-    const uint32_t w1 = __builtin_amdgcn_perm(thi, tlo, ((qw >> 2) & M) | m);
-    const uint32_t w2 = __builtin_amdgcn_perm(thi, tlo, ((qw >> 4) & M) | m);
-    const uint32_t w3 = __builtin_amdgcn_perm(thi, tlo, ((qw >> 6) & M) | m);
-    acc = __builtin_amdgcn_sdot4((int)w0, (int)x4[0], acc, false);
+    const uint32_t w0 = __builtin_amdgcn_perm(thi, tlo, and_or_fast(qw, M, m));
+    const uint32_t w1 = __builtin_amdgcn_perm(thi, tlo, and_or_fast(qw >> 2, M, m));
+    const uint32_t w2 = __builtin_amdgcn_perm(thi, tlo, and_or_fast(qw >> 4, M, m));
+    const uint32_t w3 = __builtin_amdgcn_perm(thi, tlo, and_or_fast(qw >> 6, M, m));
+    if constexpr (FIRST) acc = dot4_first(w0, x4[0]);
+    else acc = __builtin_amdgcn_sdot4((int)w0, (int)x4[0], acc, false);
     acc = __builtin_amdgcn_sdot4((int)w1, (int)x4[1], acc, false);
     acc = __builtin_amdgcn_sdot4((int)w2, (int)x4[2], acc, false);
     acc = __builtin_amdgcn_sdot4((int)w3, (int)x4[3], acc, false);
     return acc;
 }
 
+// Dot of one lane's 64 weights with its 64 fixed-point activations, before
+// the per-lane float scale (fp16 d * chunk scale * table scale).
 template <int FMT>
-__device__ __forceinline__ float row_dot(const RowData<FMT>& r, int c, const uint32_t* xh, const uint32_t* xl,
+__device__ __forceinline__ float row_dot(const RowData& r, int c, const uint32_t* xh, const uint32_t* xl,
                                          const int32_t* bsum, uint32_t tlo, uint32_t thi, const uint2* grid_s) {
     if constexpr (FMT == IQK_IQ2_K) {
         const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
-        const uint32_t sc = r.a ^ 0x8888u;               // nibble ^ 8 read as signed 4-bit = nibble - 8
+        const uint32_t sc = r.a ^ 0x8888u;  // nibble ^ 8 read as signed 4-bit = nibble - 8
         const uint32_t sx = r.b >> (4 * (c & 1));
         int ah = 0, al = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)sx, i, 1) & 0x04040404u;
-            const int h = dot16(q[i], m, tlo, thi, xh + 4 * i, 0);
-            const int l = dot16(q[i], m, tlo, thi, xl + 4 * i, 0);
+            const int h = dot16<true>(q[i], m, tlo, thi, xh + 4 * i, 0);
+            const int l = dot16<true>(q[i], m, tlo, thi, xl + 4 * i, 0);
             const int si = __builtin_amdgcn_sbfe((int)sc, 4 * i, 4);
             ah += __mul24(h, si);
             al += __mul24(l, si);
@@ -283,17 +343,17 @@ __device__ __forceinline__ float row_dot(const RowData<FMT>& r, int c, const uin
     } else if constexpr (FMT == IQK_IQ2_KS) {
         const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
         const int sh = 2 * (c & 3);
-        const uint32_t schx = ~r.b;                      // high bit flipped: 5-bit field read signed = raw - 16
+        const uint32_t schx = ~r.b;  // high bit flipped: the 5-bit field read signed = raw - 16
         int ah = 0, al = 0;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const uint32_t raw = ((r.a >> (4 * s)) & 15u) | (((schx >> (sh + s)) & 1u) << 4);
             const int si = __builtin_amdgcn_sbfe((int)raw, 0, 5);
             const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)r.c, sh + s, 1) & 0x04040404u;
-            int h = dot16(q[2 * s], m, tlo, thi, xh + 8 * s, 0);
-            h = dot16(q[2 * s + 1], m, tlo, thi, xh + 8 * s + 4, h);
-            int l = dot16(q[2 * s], m, tlo, thi, xl + 8 * s, 0);
-            l = dot16(q[2 * s + 1], m, tlo, thi, xl + 8 * s + 4, l);
+            int h = dot16<true>(q[2 * s], m, tlo, thi, xh + 8 * s, 0);
+            h = dot16<false>(q[2 * s + 1], m, tlo, thi, xh + 8 * s + 4, h);
+            int l = dot16<true>(q[2 * s], m, tlo, thi, xl + 8 * s, 0);
+            l = dot16<false>(q[2 * s + 1], m, tlo, thi, xl + 8 * s + 4, l);
             ah += __mul24(h, si);
             al += __mul24(l, si);
         }
@@ -323,45 +383,77 @@ __device__ __forceinline__ float row_dot(const RowData<FMT>& r, int c, const uin
     }
 }
 
+template <int FMT, int N>
+struct Group {
+    RowData r[Geo<N>::GIT];
+};
+
+template <int FMT, int N>
+__device__ __forceinline__ void load_group(Group<FMT, N>& g, const GemvParams& p, int64_t e_rows, int grp_row0,
+                                           int row_end, int lane_row, int c) {
+    using G = Geo<N>;
+#pragma unroll
+    for (int it = 0; it < G::GIT; ++it) {
+        // uniform first row of the iteration, clamped into the block; rows past
+        // the end re-read the last row and are not written
+        const int r0 = min(grp_row0 + it * G::RPI, row_end - 1);
+        uint32_t dl = 0;
+        if constexpr (G::LPR != 64) dl = (uint32_t)min(lane_row, row_end - 1 - r0);
+        g.r[it] = load_row<FMT, N>(p, e_rows + r0, dl, (uint32_t)c);
+    }
+}
+
 template <int FMT, int N, int XDT, bool FLOOR>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
+__global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
     using G = Geo<N>;
     __shared__ XLds<N> X;
     __shared__ uint2 grid_s[FMT == IQK_IQ1_S_R4 ? 2048 : 1];
 
+    const int nthreads = blockDim.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nwaves = nthreads >> 6;
     const int bid = blockIdx.x;
     const int pair = bid / p.nrb;
     const int rb = bid - pair * p.nrb;
     const int t = pair / p.k;
     const int j = pair - t * p.k;
     const int e = p.ids[pair];
-    const int row_begin = rb * p.rows_wg;
-    const int row_end = min(row_begin + p.rows_wg, p.out);
+    // even split of the pair's rows over its row blocks
+    const int row_begin = (int)(((int64_t)rb * p.out) / p.nrb);
+    const int row_end = (int)(((int64_t)(rb + 1) * p.out) / p.nrb);
     const int64_t out_base = (int64_t)pair * p.out;
 
     if (e < 0 || e >= p.E) {  // invalid id: NaN rows (all-ones in the floor variant)
-        for (int r = row_begin + tid; r < row_end; r += kThreads) {
+        for (int r = row_begin + tid; r < row_end; r += nthreads) {
             if constexpr (FLOOR) p.sink[out_base + r] = 0xFFFFFFFFu;
             else p.y[out_base + r] = __builtin_nanf("");
         }
         return;
     }
 
+    const int c = lane % G::LPR;  // chunk of k owned by this lane
+    const int lane_row = lane / G::LPR;
+    const int64_t e_rows = (int64_t)e * p.out;
+    // Reduction groups of the block are dealt round-robin to the waves, so
+    // the four SIMDs (waves w, w+4, ...) get equal shares of the work.
+    const int nblk_groups = (row_end - row_begin + G::RPG - 1) / G::RPG;
+    auto grp_row = [&](int i) { return row_begin + (wave + i * nwaves) * G::RPG; };
+    const int my_groups = wave < nblk_groups ? (nblk_groups - wave + nwaves - 1) / nwaves : 0;
+
+    // the activation is on the critical path: request it first
     const int64_t xoff = ((int64_t)t * p.x_slots + (p.x_slots == 1 ? 0 : j)) * N;
     const void* xrow = XDT == IQK_BF16 ? (const void*)((const uint16_t*)p.x + xoff) : (const void*)((const float*)p.x + xoff);
-    prep_x<FMT, N, XDT>(xrow, X, tid);
+
+    for (int b = tid; b < N / 16; b += nthreads) prep_block<FMT, N, XDT>(xrow, X, b);
     if constexpr (FMT == IQK_IQ1_S_R4) {
         const uint4* src = (const uint4*)p.grid;
         uint4* dst = (uint4*)grid_s;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[tid + kThreads * i] = src[tid + kThreads * i];
+        for (int i = tid; i < 1024; i += nthreads) dst[i] = src[i];
     }
-    __syncthreads();
+    lds_barrier();
 
-    const int c = lane % G::LPR;  // chunk of k owned by this lane
     uint32_t xh[16], xl[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -370,33 +462,29 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
         xh[4 * i] = a.x; xh[4 * i + 1] = a.y; xh[4 * i + 2] = a.z; xh[4 * i + 3] = a.w;
         xl[4 * i] = b.x; xl[4 * i + 1] = b.y; xl[4 * i + 2] = b.z; xl[4 * i + 3] = b.w;
     }
+    // The first two groups of rows are requested only now: issued earlier, the
+    // whole launch's row traffic would queue ahead of the activation reads and
+    // hold every wave at the barrier until most rows had streamed in.
+    Group<FMT, N> bufA, bufB;
+    if (my_groups > 0) load_group<FMT, N>(bufA, p, e_rows, grp_row(0), row_end, lane_row, c);
+    if (my_groups > 1) load_group<FMT, N>(bufB, p, e_rows, grp_row(1), row_end, lane_row, c);
     const float lane_scale = X.scale[c] * p.tab_scale;
     int32_t bsum[2] = {0, 0};
     if constexpr (FMT == IQK_IQ1_S_R4) {
         bsum[0] = X.bsum[2 * c];
         bsum[1] = X.bsum[2 * c + 1];
     }
-    const int lane_row = lane / G::LPR;
-    const int64_t e_rows = (int64_t)e * p.out;
 
-    for (int g = 0; g < p.groups; ++g) {
-        const int grp_row0 = row_begin + (wave * p.groups + g) * G::RPG;
-        if (grp_row0 >= row_end) break;
-        RowData<FMT> rd[G::GIT];
-#pragma unroll
-        for (int it = 0; it < G::GIT; ++it) {
-            const int r = min(grp_row0 + it * G::RPI + lane_row, row_end - 1);
-            rd[it] = load_row<FMT, N>(p, e_rows + r, c);
-        }
+    auto process = [&](const Group<FMT, N>& gb, int grp_row0) {
         uint32_t part[G::GIT];
 #pragma unroll
         for (int it = 0; it < G::GIT; ++it) {
             if constexpr (FLOOR) {
-                part[it] = rd[it].q.x ^ rd[it].q.y ^ rd[it].q.z ^ rd[it].q.w ^ rd[it].a ^ (rd[it].b << 8) ^
-                           (rd[it].c << 16) ^ (rd[it].d << 3) ^ xh[it & 15];
+                part[it] = gb.r[it].q.x ^ gb.r[it].q.y ^ gb.r[it].q.z ^ gb.r[it].q.w ^ gb.r[it].a ^
+                           (gb.r[it].b << 8) ^ (gb.r[it].c << 16) ^ (gb.r[it].d << 3) ^ xh[it & 15];
             } else {
-                const float f = row_dot<FMT>(rd[it], c, xh, xl, bsum, p.tab_lo, p.tab_hi, grid_s);
-                part[it] = __float_as_uint(f * (half_to_float(rd[it].d) * lane_scale));
+                const float f = row_dot<FMT>(gb.r[it], c, xh, xl, bsum, p.tab_lo, p.tab_hi, grid_s);
+                part[it] = __float_as_uint(f * (half_to_float(gb.r[it].d) * lane_scale));
             }
         }
         int row_in_grp;
@@ -407,24 +495,37 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
             if constexpr (FLOOR) p.sink[out_base + r] = sum;
             else p.y[out_base + r] = __uint_as_float(sum);
         }
+    };
+
+    for (int i = 0; i < my_groups; i += 2) {
+        process(bufA, grp_row(i));
+        if (i + 2 < my_groups) load_group<FMT, N>(bufA, p, e_rows, grp_row(i + 2), row_end, lane_row, c);
+        if (i + 1 >= my_groups) break;
+        process(bufB, grp_row(i + 1));
+        if (i + 3 < my_groups) load_group<FMT, N>(bufB, p, e_rows, grp_row(i + 3), row_end, lane_row, c);
     }
 }
 
 template <int FMT, int N, int XDT, bool FLOOR>
 hipError_t launch_inst(GemvParams p, int64_t pairs, hipStream_t s) {
     using G = Geo<N>;
-    // about two workgroups per CU over the whole call, each wave keeping
-    // at least one reduction group
-    int64_t bpp = (512 + pairs - 1) / pairs;
-    int64_t rows = (p.out + bpp - 1) / bpp;
-    int64_t groups = (rows + kWaves * G::RPG - 1) / (kWaves * G::RPG);
-    groups = groups < 1 ? 1 : (groups > 16 ? 16 : groups);
-    p.groups = (int32_t)groups;
-    p.rows_wg = (int32_t)(groups * kWaves * G::RPG);
-    p.nrb = (int32_t)((p.out + p.rows_wg - 1) / p.rows_wg);
-    const int64_t blocks = pairs * p.nrb;
+    // one large workgroup per CU over the whole call: split each pair's rows
+    // into nrb blocks with pairs * nrb <= 256, each block a few row groups per wave
+    int64_t nrb = IQK_GEMV_TARGET_BLOCKS / (pairs > 0 ? pairs : 1);
+    const int64_t max_nrb = (p.out + G::RPG - 1) / G::RPG;
+    nrb = nrb < 1 ? 1 : (nrb > max_nrb ? max_nrb : nrb);
+    const int64_t rows = (p.out + nrb - 1) / nrb;           // rows of the largest block
+    const int64_t groups = (rows + G::RPG - 1) / G::RPG;    // reduction groups per block
+    // waves: a multiple of four (one share per SIMD) up to 16, at least
+    // IQK_GEMV_MIN_GROUPS groups each once the block is large enough
+    int64_t waves = (groups + IQK_GEMV_MIN_GROUPS - 1) / IQK_GEMV_MIN_GROUPS;
+    waves = groups < 4 ? groups : ((waves + 3) / 4) * 4;
+    waves = waves > kMaxWaves ? kMaxWaves : (waves < 1 ? 1 : waves);
+    p.nrb = (int32_t)nrb;
+    p.groups = 0;
+    const int64_t blocks = pairs * nrb;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gemv_kernel<FMT, N, XDT, FLOOR>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gemv_kernel<FMT, N, XDT, FLOOR>), dim3((unsigned)blocks), dim3((unsigned)(64 * waves)), 0, s, p);
     return hipGetLastError();
 }
 
@@ -470,7 +571,7 @@ hipError_t launch_gemv(const GemvLaunch& a, bool floor_variant, hipStream_t s) {
     p.ids = a.ids;
     p.y = a.y;
     p.sink = a.sink;
-    p.nrb = p.groups = p.rows_wg = 0;
+    p.nrb = p.groups = 0;
     const int64_t pairs = a.T * a.k;
     return floor_variant ? launch_fmt<true>(p, a.fmt, a.n, a.x_dtype, pairs, s)
                          : launch_fmt<false>(p, a.fmt, a.n, a.x_dtype, pairs, s);
