@@ -47,7 +47,10 @@ namespace {
 #ifndef IQK_GEMV_MIN_GROUPS
 #define IQK_GEMV_MIN_GROUPS 2       // reduction groups per wave when the block has >= 8
 #endif
-constexpr int kMaxWaves = 16;
+#ifndef IQK_GEMV_MAX_WAVES
+#define IQK_GEMV_MAX_WAVES 16        // waves per workgroup (launch bound)
+#endif
+constexpr int kMaxWaves = IQK_GEMV_MAX_WAVES;
 
 struct GemvParams {
     const uint8_t* S;
@@ -162,30 +165,45 @@ struct XLds {
     int32_t bsum[N / 32];
 };
 
-// Convert one 16-value block of the activation (block index b; the four
-// blocks of a 64-value chunk sit in four consecutive lanes).
-template <int FMT, int N, int XDT>
-__device__ __forceinline__ void prep_block(const void* xrow, XLds<N>& L, int b) {
-    float v[16];
+// Raw activation words of one 16-value block (bf16: 8 words, f32: 16).
+template <int XDT>
+struct XRaw {
+    uint32_t w[XDT == IQK_BF16 ? 8 : 16];
+};
+
+template <int N, int XDT>
+__device__ __forceinline__ XRaw<XDT> load_xblock(const void* xrow, int b) {
+    XRaw<XDT> r;
     if constexpr (XDT == IQK_BF16) {
         const uint4* src = (const uint4*)xrow + 2 * b;
         const uint4 a = src[0], c = src[1];
-        const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            v[2 * i] = __uint_as_float(w[i] << 16);
-            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-        }
+        r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+        r.w[4] = c.x; r.w[5] = c.y; r.w[6] = c.z; r.w[7] = c.w;
     } else {
-        const float4* src = (const float4*)xrow + 4 * b;
+        const uint4* src = (const uint4*)xrow + 4 * b;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float4 f = src[i];
-            v[4 * i] = f.x;
-            v[4 * i + 1] = f.y;
-            v[4 * i + 2] = f.z;
-            v[4 * i + 3] = f.w;
+            const uint4 f = src[i];
+            r.w[4 * i] = f.x; r.w[4 * i + 1] = f.y; r.w[4 * i + 2] = f.z; r.w[4 * i + 3] = f.w;
         }
+    }
+    return r;
+}
+
+// Convert one 16-value block of the activation (block index b; the four
+// blocks of a 64-value chunk sit in four consecutive lanes).
+template <int FMT, int N, int XDT>
+__device__ __forceinline__ void prep_block(const XRaw<XDT>& raw, XLds<N>& L, int b) {
+    float v[16];
+    if constexpr (XDT == IQK_BF16) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[2 * i] = __uint_as_float(raw.w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(raw.w[i] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(raw.w[i]);
     }
     uint32_t amax = 0;
 #pragma unroll
@@ -294,17 +312,11 @@ __device__ __forceinline__ int dot4_first(uint32_t a, uint32_t b) {
     return d;
 }
 
-// (a & b) | c in one v_bitop3_b32.  The truth table is indexed by
-// (a << 2) | (b << 1) | c, so (a & b) | c is 0xEA.  On gfx950 the bitop3
-// issues at the rate of the two-operand bitwise ops, about twice the rate of
-// v_and_or_b32.
-__device__ __forceinline__ uint32_t and_or_fast(uint32_t a, uint32_t b, uint32_t c) {
-    uint32_t d;
-    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0xea" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-    return d;
-}
+// (a & b) | c, left to the compiler (measured faster in context than a
+// hand-placed v_bitop3_b32).
+__device__ __forceinline__ uint32_t and_or_fast(uint32_t a, uint32_t b, uint32_t c) { return (a & b) | c; }
 
-// 16 weights of one code word against 4 activation words.
+// 16 weights of one code word against 4 activation words, as one chain.
 template <bool FIRST>
 __device__ __forceinline__ int dot16(uint32_t qw, uint32_t m, uint32_t tlo, uint32_t thi, const uint32_t* x4, int acc) {
     const uint32_t M = 0x03030303u;
@@ -329,15 +341,35 @@ __device__ __forceinline__ float row_dot(const RowData& r, int c, const uint32_t
         const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
         const uint32_t sc = r.a ^ 0x8888u;  // nibble ^ 8 read as signed 4-bit = nibble - 8
         const uint32_t sx = r.b >> (4 * (c & 1));
-        int ah = 0, al = 0;
+        // all four sub-blocks' weights first, then eight interleaved dot
+        // chains (hi/lo x 4 sub-blocks), so dependent ops are not adjacent
+        uint32_t w[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)sx, i, 1) & 0x04040404u;
-            const int h = dot16<true>(q[i], m, tlo, thi, xh + 4 * i, 0);
-            const int l = dot16<true>(q[i], m, tlo, thi, xl + 4 * i, 0);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                w[i][jj] = __builtin_amdgcn_perm(thi, tlo, and_or_fast(q[i] >> (2 * jj), 0x03030303u, m));
+        }
+        int h[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            h[i] = dot4_first(w[i][0], xh[4 * i]);
+            l[i] = dot4_first(w[i][0], xl[4 * i]);
+        }
+#pragma unroll
+        for (int jj = 1; jj < 4; ++jj)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                h[i] = __builtin_amdgcn_sdot4((int)w[i][jj], (int)xh[4 * i + jj], h[i], false);
+                l[i] = __builtin_amdgcn_sdot4((int)w[i][jj], (int)xl[4 * i + jj], l[i], false);
+            }
+        int ah = 0, al = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
             const int si = __builtin_amdgcn_sbfe((int)sc, 4 * i, 4);
-            ah += __mul24(h, si);
-            al += __mul24(l, si);
+            ah += __mul24(h[i], si);
+            al += __mul24(l[i], si);
         }
         return (float)ah * 256.0f + (float)al;
     } else if constexpr (FMT == IQK_IQ2_KS) {
@@ -446,7 +478,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
     const int64_t xoff = ((int64_t)t * p.x_slots + (p.x_slots == 1 ? 0 : j)) * N;
     const void* xrow = XDT == IQK_BF16 ? (const void*)((const uint16_t*)p.x + xoff) : (const void*)((const float*)p.x + xoff);
 
-    for (int b = tid; b < N / 16; b += nthreads) prep_block<FMT, N, XDT>(xrow, X, b);
+    for (int b = tid; b < N / 16; b += nthreads) prep_block<FMT, N, XDT>(load_xblock<N, XDT>(xrow, b), X, b);
     if constexpr (FMT == IQK_IQ1_S_R4) {
         const uint4* src = (const uint4*)p.grid;
         uint4* dst = (uint4*)grid_s;
