@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Routed-expert decode benchmark on one MI355X.
 
-Workload (default): IQ2_K routed MoE decode, 1 token, top-6 of 256 experts,
+Headline workload: IQ2_K routed MoE decode, 1 token, top-6 of 256 experts,
 gate and up [2048, 4096] stored as one fused [4096, 4096] tensor per expert,
 down [4096, 2048]; activation bf16 N(0,1); fp16 super-block scales
 |N(0,1)| * 0.01; codes, scale indices and alphabet bits uniform ("mlx-iqk"
@@ -12,13 +12,18 @@ bf16 [1, 6, 2048] tensor; the SwiGLU between them is outside this path).
 Timing: inputs are resident in HBM before timing.  Weights are rotated over
 8 independent pools (each step uses the next pool and fresh expert ids) so no
 step can be served from the 256 MiB last-level cache.  S steps are captured
-into one HIP graph and replayed; W warmup steps, then K timed steps between
-two synchronizations, HIP events on the launch stream.  Value = algorithmic
-bytes (compressed bytes of the distinct selected experts + x + y) / time.
+into one HIP graph and replayed; W warmup steps, then exactly K timed steps
+between two synchronizations, HIP events on the launch stream.  Value =
+algorithmic bytes (compressed bytes of the distinct selected experts + x + y)
+per second.
 
-`roofline` reports the dominant kernel (the gate/up matvec): its algorithmic
+`roofline` reports the dominant kernel (the gate/up matvec): algorithmic
 bytes per launch over its average launch duration, from a graph of that
-kernel alone.  `cpu_baseline` times the CPU oracle on one full decode step.
+kernel alone.  `cells` (default on) adds every format x projection x token
+count of the workload family, each with its deleted-decode floor and a plain
+streaming read of the same byte count, plus the prefill rows (routing,
+dequantization producer, MFMA grouped GEMM) at 512 tokens.  `cpu_baseline`
+times the CPU oracle on whole decode steps (about 10 s of CPU work).
 """
 from __future__ import annotations
 
@@ -34,7 +39,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
 POOLS = 8
+E, K, H, I = 256, 6, 4096, 2048
+FMT_NAME = {1: "IQ2_KS", 2: "IQ2_K", 3: "IQ1_S_R4"}
 
 
 def _parse():
@@ -42,40 +50,41 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--cells", choices=["headline", "all"], default="headline")
+    ap.add_argument("--cells", choices=["none", "all"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=2)
     return ap.parse_args()
 
 
+def log(msg):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
 class Pools:
     """Expert-stacked stream tensors of one projection, replicated over pools."""
 
-    def __init__(self, q, torch, fmt, E, out, n, seed, pools=POOLS):
+    def __init__(self, q, torch, fmt, out, n, seed, pools=POOLS):
         import synth
-        t0 = time.time()
         wire = synth.wire(fmt, E * out, n, seed)
         streams = q.pack_relayout(fmt, wire, E * out, n)
         self.host_streams = streams
         base = torch.from_numpy(streams).cuda()
-        self.w = [q.Weights(fmt, E, out, n, base)]
-        for _ in range(pools - 1):
-            self.w.append(q.Weights(fmt, E, out, n, base.clone()))
-        self.fmt, self.E, self.out, self.n = fmt, E, out, n
+        self.w = [q.Weights(fmt, E, out, n, base)] + [q.Weights(fmt, E, out, n, base.clone()) for _ in range(pools - 1)]
+        self.fmt, self.out, self.n = fmt, out, n
         self.row_bytes = q.row_bytes(fmt, n)
-        self.setup_s = time.time() - t0
 
     def bytes_for(self, ids: np.ndarray) -> int:
         """algorithmic weight bytes: every distinct selected expert once"""
         return len(np.unique(ids)) * self.out * self.row_bytes
 
 
-def _timed_graph(torch, fn, S, reps, warm_reps):
+def timed_graph(torch, fn, S, reps, warm_reps):
     """Capture S calls of fn(i) in one graph; replay; return ms per call."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        for i in range(S):  # eager pass (also validates launches before capture)
+        for i in range(S):  # eager pass: every launch is checked before capture
             fn(i)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
@@ -94,7 +103,168 @@ def _timed_graph(torch, fn, S, reps, warm_reps):
         g.replay()
     e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / (reps * S), g
+    return e0.elapsed_time(e1) / (reps * S)
+
+
+def timed_eager(torch, fn, reps, warm):
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+class Ctx:
+    def __init__(self, q, torch, seed):
+        import synth
+        self.q, self.torch = q, torch
+        self.values = synth.values_table(seed + 1)
+        self.grid_host = synth.ternary_grid(seed + 4)
+        self.grid = torch.from_numpy(self.grid_host).cuda()
+        self.sbuf = None
+        self.ssink = torch.zeros(1 << 14, dtype=torch.int32, device="cuda")
+
+    def stream_ms(self, nbytes, S, reps, warm):
+        nb = int(nbytes) // 16 * 16
+        slots = 16
+        need = nb * slots
+        if self.sbuf is None or self.sbuf.numel() < need:
+            self.sbuf = None
+            self.sbuf = self.torch.empty(need, dtype=self.torch.uint8, device="cuda")
+            self.sbuf.fill_(1)
+
+        def sread(i):
+            self.q.stream_read(self.sbuf[(i % slots) * nb:(i % slots + 1) * nb], self.ssink)
+
+        return timed_graph(self.torch, sread, S, reps, warm)
+
+
+def validate_sample(oracle, pool, ids, xin, y, slots, values, grid_host, rng, rows_per=48):
+    """worst |y - y_exact| / sum|w x| over sampled rows of every selected expert"""
+    worst = 0.0
+    yv = y.cpu().numpy()
+    T, k = ids.shape
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            for r in rng.choice(pool.out, rows_per, replace=False):
+                w = oracle.dequant(pool.fmt, pool.host_streams, E * pool.out, pool.n, values, grid_host,
+                                   oracle.F32, r0=e * pool.out + int(r), nr=1)[0].astype(np.float64)
+                xx = (xin[t, 0] if slots == 1 else xin[t, j]).astype(np.float64)
+                ref = float(w @ xx)
+                scale = float(np.abs(w) @ np.abs(xx))
+                worst = max(worst, abs(float(yv[t, j, r]) - ref) / max(scale, 1e-30))
+    return worst
+
+
+def decode_cell(ctx, pool, T, proj, S, reps, warm, seed):
+    """one matvec cell: kernel time, floor time, stream-read time for the same bytes"""
+    import synth
+    import oracle
+    q, torch = ctx.q, ctx.torch
+    slots = 1 if proj == "gate_up" else K
+    ids_host = [synth.topk_ids(T, K, E, seed * 1000 + i) for i in range(S)]
+    ids = [torch.from_numpy(a).cuda() for a in ids_host]
+    x = torch.from_numpy(synth.normal((T, slots, pool.n), seed + 7)).to(torch.bfloat16).cuda()
+    y = torch.empty((T, K, pool.out), dtype=torch.float32, device="cuda")
+    sink = torch.empty((T, K, pool.out), dtype=torch.int32, device="cuda")
+    grid = ctx.grid if pool.fmt == 3 else None
+    q.moe_gemv(pool.w[0], x, ids[0], ctx.values, grid, x_slots=slots, y=y)
+    torch.cuda.synchronize()
+    worst = validate_sample(oracle, pool, ids_host[0], x.float().cpu().numpy(), y, slots, ctx.values,
+                            ctx.grid_host, np.random.default_rng(seed), rows_per=8)
+
+    def run(i):
+        q.moe_gemv(pool.w[i % POOLS], x, ids[i], ctx.values, grid, x_slots=slots, y=y)
+
+    def run_floor(i):
+        q.floor_gemv(pool.w[i % POOLS], x, ids[i], ctx.values, grid, x_slots=slots, sink=sink)
+
+    ms = timed_graph(torch, run, S, reps, warm)
+    ms_floor = timed_graph(torch, run_floor, S, reps, warm)
+    nbytes = float(np.mean([pool.bytes_for(a) for a in ids_host])) + x.numel() * 2 + y.numel() * 4
+    ms_stream = ctx.stream_ms(nbytes, S, reps, warm)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"cell": f"{FMT_NAME[pool.fmt]} {proj} T={T}", "kind": "decode", "us": round(ms * 1e3, 3),
+            "bytes": int(nbytes), "GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "floor_us": round(ms_floor * 1e3, 3), "ratio_to_floor": round(ms / ms_floor, 3),
+            "stream_read_us": round(ms_stream * 1e3, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "validation_worst": worst}
+
+
+def prefill_cells(ctx, fmt, seed):
+    """routing + producer + grouped GEMM at 512 tokens for gate/up and down"""
+    import synth
+    import oracle
+    q, torch = ctx.q, ctx.torch
+    T = 512
+    out = []
+    ids_h = synth.topk_ids(T, K, E, seed + 11)
+    ids = torch.from_numpy(ids_h).cuda()
+    counts, offsets, perm = q.route(ids, E)
+    route_ms = timed_eager(torch, lambda i: q.route(ids, E), 50, 5)
+    total_ms = route_ms
+    out.append({"cell": f"{FMT_NAME[fmt]} prefill route T=512", "kind": "route", "us": round(route_ms * 1e3, 3)})
+    grid = ctx.grid if fmt == 3 else None
+    for proj, (rows, n) in (("gate_up", (2 * I, H)), ("down", (H, I))):
+        slots = 1 if proj == "gate_up" else K
+        wire = synth.wire(fmt, E * rows, n, seed + (1 if proj == "gate_up" else 2))
+        streams_h = q.pack_relayout(fmt, wire, E * rows, n)
+        del wire
+        w = q.Weights(fmt, E, rows, n, torch.from_numpy(streams_h).cuda())
+        dense = torch.empty((E, rows, n), dtype=torch.bfloat16, device="cuda")
+        x = torch.from_numpy(synth.normal((T, slots, n), seed + 5)).to(torch.bfloat16).cuda()
+        y = torch.zeros((T, K, rows), dtype=torch.float32, device="cuda")
+        q.dequant(w, ctx.values, grid, torch.bfloat16, out=dense.view(E * rows, n))
+        q.grouped_gemm(dense, x, T, K, offsets, perm, x_slots=slots, y=y)
+        torch.cuda.synchronize()
+        # validation on sampled outputs against the float32-weight oracle
+        rng = np.random.default_rng(seed)
+        xv = x.float().cpu().numpy()
+        yv = y.cpu().numpy()
+        worst = 0.0
+        for _ in range(24):
+            t, j = int(rng.integers(T)), int(rng.integers(K))
+            e = int(ids_h[t, j])
+            r = int(rng.integers(rows))
+            wr = oracle.dequant(fmt, streams_h, E * rows, n, ctx.values, ctx.grid_host, oracle.F32,
+                                r0=e * rows + r, nr=1)[0].astype(np.float64)
+            xx = (xv[t, 0] if slots == 1 else xv[t, j]).astype(np.float64)
+            worst = max(worst, abs(float(yv[t, j, r]) - float(wr @ xx)) / max(float(np.abs(wr) @ np.abs(xx)), 1e-30))
+        wbytes = E * rows * q.row_bytes(fmt, n)
+        dbytes = E * rows * n * 2
+        dv = dense.view(E * rows, n)
+        prod_ms = timed_eager(torch, lambda i: q.dequant(w, ctx.values, grid, torch.bfloat16, out=dv), 10, 2)
+        floor_ms = timed_eager(torch, lambda i: q.floor_dequant(w, torch.bfloat16, out=dv), 10, 2)
+        pbytes = wbytes + dbytes
+        pg = pbytes / (prod_ms * 1e-3) / 1e9
+        out.append({"cell": f"{FMT_NAME[fmt]} prefill producer {proj}", "kind": "producer",
+                    "us": round(prod_ms * 1e3, 1), "bytes": int(pbytes), "GBps": round(pg, 1),
+                    "frac_hbm": round(pg / HBM_PEAK_GBS, 4), "floor_us": round(floor_ms * 1e3, 1),
+                    "ratio_to_floor": round(prod_ms / floor_ms, 3)})
+        gemm_ms = timed_eager(torch, lambda i: q.grouped_gemm(dense, x, T, K, offsets, perm, x_slots=slots, y=y),
+                              10, 2)
+        gbytes = dbytes + x.numel() * 2 + y.numel() * 4
+        flops = 2.0 * T * K * rows * n
+        gg = gbytes / (gemm_ms * 1e-3) / 1e9
+        tf = flops / (gemm_ms * 1e-3) / 1e12
+        out.append({"cell": f"{FMT_NAME[fmt]} prefill grouped GEMM {proj}", "kind": "gemm",
+                    "us": round(gemm_ms * 1e3, 1), "bytes": int(gbytes), "GBps": round(gg, 1),
+                    "frac_hbm": round(gg / HBM_PEAK_GBS, 4), "TFLOPs": round(tf, 2),
+                    "mfma_util": round(tf / BF16_PEAK_TFLOPS, 4), "validation_worst": worst})
+        total_ms += prod_ms + gemm_ms
+        del dense, w, y, dv
+        torch.cuda.empty_cache()
+    out.append({"cell": f"{FMT_NAME[fmt]} prefill total (route + 2 x (producer + GEMM))", "kind": "prefill",
+                "us": round(total_ms * 1e3, 1), "tokens_per_s": round(T / (total_ms * 1e-3), 1)})
+    return out
 
 
 def main():
@@ -108,45 +278,36 @@ def main():
     import torch
     import dequant_iqk_moe_amd as q
     import synth
+    import oracle
 
     torch.cuda.set_device(0)
-    fmt = q.IQ2_K
-    E, T, k, H, I = 256, 1, 6, 4096, 2048
+    T = 1
     # steps per captured graph: the largest divisor of K up to 64, so exactly K steps are timed
     S = max(d for d in range(1, 65) if args.steps % d == 0)
+    reps = args.steps // S
+    warm = max(1, -(-args.warmup // S))
     t0 = time.time()
-    gate_up = Pools(q, torch, fmt, E, 2 * I, H, args.seed)
-    down = Pools(q, torch, fmt, E, H, I, args.seed + 100)
-    values = synth.values_table(args.seed + 1)
-    ids_host = [synth.topk_ids(T, k, E, 10_000 + i) for i in range(S)]
+    ctx = Ctx(q, torch, args.seed)
+    gate_up = Pools(q, torch, q.IQ2_K, 2 * I, H, args.seed)
+    down = Pools(q, torch, q.IQ2_K, H, I, args.seed + 100)
+    values = ctx.values
+    ids_host = [synth.topk_ids(T, K, E, 10_000 + i) for i in range(S)]
     ids_dev = [torch.from_numpy(a).cuda() for a in ids_host]
     x = torch.from_numpy(synth.normal((T, H), args.seed + 2)).to(torch.bfloat16).cuda()
-    h = torch.from_numpy(synth.normal((T, k, I), args.seed + 3)).to(torch.bfloat16).cuda()
-    y1 = torch.empty((T, k, 2 * I), dtype=torch.float32, device="cuda")
-    y2 = torch.empty((T, k, H), dtype=torch.float32, device="cuda")
+    h = torch.from_numpy(synth.normal((T, K, I), args.seed + 3)).to(torch.bfloat16).cuda()
+    y1 = torch.empty((T, K, 2 * I), dtype=torch.float32, device="cuda")
+    y2 = torch.empty((T, K, H), dtype=torch.float32, device="cuda")
     setup_s = time.time() - t0
 
     # validation on the exact timed inputs before any timing (sampled rows)
-    import oracle
     q.moe_gemv(gate_up.w[0], x, ids_dev[0], values, y=y1)
-    q.moe_gemv(down.w[0], h, ids_dev[0], values, x_slots=k, y=y2)
+    q.moe_gemv(down.w[0], h, ids_dev[0], values, x_slots=K, y=y2)
     torch.cuda.synchronize()
     rng = np.random.default_rng(7)
-    xv = x.float().cpu().numpy()
+    xv = x.float().cpu().numpy().reshape(T, 1, H)
     hv = h.float().cpu().numpy()
-    worst = 0.0
-    for pj, (pool, xin, yv, slots) in enumerate(((gate_up, xv, y1, 1), (down, hv, y2, k))):
-        ygot = yv.cpu().numpy()
-        for j in range(k):
-            e = int(ids_host[0][0, j])
-            rows = rng.choice(pool.out, 64, replace=False)
-            for r in rows:
-                wrow = oracle.dequant(fmt, pool.host_streams, E * pool.out, pool.n, values, None,
-                                      oracle.F32, r0=e * pool.out + int(r), nr=1)[0].astype(np.float64)
-                xx = xin[0] if slots == 1 else xin[0, j]
-                ref = float(wrow @ xx.astype(np.float64))
-                scale = float(np.abs(wrow) @ np.abs(xx.astype(np.float64)))
-                worst = max(worst, abs(float(ygot[0, j, r]) - ref) / max(scale, 1e-30))
+    worst = max(validate_sample(oracle, gate_up, ids_host[0], xv, y1, 1, values, None, rng),
+                validate_sample(oracle, down, ids_host[0], hv, y2, K, values, None, rng))
     if worst > 1e-3:
         print(json.dumps({"error": f"validation failed: worst sampled error {worst:.3e}"}))
         sys.exit(1)
@@ -154,67 +315,81 @@ def main():
     def step(i):
         p = i % POOLS
         q.moe_gemv(gate_up.w[p], x, ids_dev[i], values, y=y1)
-        q.moe_gemv(down.w[p], h, ids_dev[i], values, x_slots=k, y=y2)
+        q.moe_gemv(down.w[p], h, ids_dev[i], values, x_slots=K, y=y2)
 
-    reps = args.steps // S
-    warm = max(1, -(-args.warmup // S))
-    ms_step, _ = _timed_graph(torch, step, S, reps, warm)
-    steps_timed = reps * S
-
-    bytes_steps = []
-    for i in range(S):
-        b = gate_up.bytes_for(ids_host[i]) + down.bytes_for(ids_host[i])
-        b += x.numel() * 2 + y1.numel() * 4 + h.numel() * 2 + y2.numel() * 4
-        bytes_steps.append(b)
+    ms_step = timed_graph(torch, step, S, reps, warm)
+    bytes_steps = [gate_up.bytes_for(a) + down.bytes_for(a) + x.numel() * 2 + y1.numel() * 4 + h.numel() * 2
+                   + y2.numel() * 4 for a in ids_host]
     bytes_per_step = float(np.mean(bytes_steps))
     gbs = bytes_per_step / (ms_step * 1e-3) / 1e9
+    log(f"headline step: {ms_step * 1e3:.2f} us, {gbs:.1f} GB/s")
 
-    # dominant kernel: the gate/up matvec alone
+    # dominant kernel: the gate/up matvec alone, its floor and a same-size streaming read
     def gu(i):
         q.moe_gemv(gate_up.w[i % POOLS], x, ids_dev[i], values, y=y1)
 
-    ms_gu, _ = _timed_graph(torch, gu, S, reps, warm)
+    ms_gu = timed_graph(torch, gu, S, reps, warm)
     gu_bytes = float(np.mean([gate_up.bytes_for(a) + x.numel() * 2 + y1.numel() * 4 for a in ids_host]))
     gu_gbs = gu_bytes / (ms_gu * 1e-3) / 1e9
-
-    # its deleted-decode floor (same loads, no decode)
-    sink = torch.empty((T, k, 2 * I), dtype=torch.int32, device="cuda")
+    sink = torch.empty((T, K, 2 * I), dtype=torch.int32, device="cuda")
 
     def gu_floor(i):
         q.floor_gemv(gate_up.w[i % POOLS], x, ids_dev[i], values, sink=sink)
 
-    ms_floor, _ = _timed_graph(torch, gu_floor, S, reps, warm)
+    ms_floor = timed_graph(torch, gu_floor, S, reps, warm)
+    ms_stream = ctx.stream_ms(gu_bytes, S, reps, warm)
 
-    # plain streaming read of the same byte count (floor-rate reference)
-    nb = int(gu_bytes) // 16 * 16
-    slots = 64
-    sbuf = torch.empty(nb * slots, dtype=torch.uint8, device="cuda")
-    sbuf.fill_(1)
-    ssink = torch.zeros(1 << 14, dtype=torch.int32, device="cuda")
-
-    def sread(i):
-        q.stream_read(sbuf[(i % slots) * nb:(i % slots + 1) * nb], ssink)
-
-    ms_stream, _ = _timed_graph(torch, sread, S, reps, warm)
-    del sbuf
+    cells = []
+    if args.cells == "all":
+        Sc, rc, wc = 32, 8, 2
+        cells.append(decode_cell(ctx, gate_up, 1, "gate_up", Sc, rc, wc, 21))
+        cells.append(decode_cell(ctx, down, 1, "down", Sc, rc, wc, 22))
+        for fmt, Ts, sd in ((q.IQ2_KS, (1, 8), 3), (q.IQ1_S_R4, (1,), 4)):
+            pg = Pools(q, torch, fmt, 2 * I, H, 100 + sd)
+            pd = Pools(q, torch, fmt, H, I, 200 + sd)
+            for Tt in Ts:
+                cells.append(decode_cell(ctx, pg, Tt, "gate_up", Sc, rc, wc, 30 + sd + Tt))
+                cells.append(decode_cell(ctx, pd, Tt, "down", Sc, rc, wc, 40 + sd + Tt))
+            del pg, pd
+            torch.cuda.empty_cache()
+        # the single-matrix case: IQ2_KS [256, 512], fp32 activation, E = 1, k = 1
+        w1 = q.Weights.from_wire(q.IQ2_KS, 1, 256, 512, synth.wire(q.IQ2_KS, 256, 512, 1))
+        x1 = torch.from_numpy(synth.normal((1, 512), 1)).cuda()
+        id1 = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
+        y1s = torch.empty((1, 1, 256), dtype=torch.float32, device="cuda")
+        ms1 = timed_graph(torch, lambda i: q.moe_gemv(w1, x1, id1, values, y=y1s), Sc, rc, wc)
+        b1 = 256 * q.row_bytes(q.IQ2_KS, 512) + 512 * 4 + 256 * 4
+        cells.append({"cell": "IQ2_KS single [256,512] fp32 x", "kind": "decode", "us": round(ms1 * 1e3, 3),
+                      "bytes": b1, "GBps": round(b1 / (ms1 * 1e-3) / 1e9, 2)})
+        ctx.sbuf = None
+        torch.cuda.empty_cache()
+        for fmt in (q.IQ2_K, q.IQ2_KS):
+            cells.extend(prefill_cells(ctx, fmt, 500 + fmt))
+        for c in cells:
+            log(json.dumps(c))
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle as orc
+        # whole decode steps through the single-threaded oracle, about 10 s of CPU work
         t1 = time.perf_counter()
-        orc.moe(fmt, gate_up.host_streams, E, 2 * I, H, xv.reshape(T, 1, H), ids_host[0], values)
-        orc.moe(fmt, down.host_streams, E, H, I, hv.reshape(T, k, I), ids_host[0], values, x_slots=k)
+        nsteps, nbytes = 0, 0
+        while nsteps < 1 or (time.perf_counter() - t1 < 10.0 and nsteps < len(ids_host)):
+            a = ids_host[nsteps]
+            oracle.moe(q.IQ2_K, gate_up.host_streams, E, 2 * I, H, xv, a, values)
+            oracle.moe(q.IQ2_K, down.host_streams, E, H, I, hv, a, values, x_slots=K)
+            nbytes += bytes_steps[nsteps]
+            nsteps += 1
         dt = time.perf_counter() - t1
-        cpu = {"value": round(bytes_steps[0] / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": "one full decode step (T=1: gate/up and down matvecs of 6 experts) through the "
-                         f"single-threaded C oracle, {dt:.1f} s"}
+        cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{nsteps} full decode steps (T=1: gate/up and down matvecs of 6 experts each) "
+                         f"through the single-threaded C oracle in {dt:.1f} s"}
 
     result = {
         "metric": "routed-expert decode GB/s and ratio to HBM floor per format/projection",
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": steps_timed,
+        "steps": reps * S,
         "warmup": warm * S,
         "ms_per_step": round(ms_step, 6),
         "higher_is_better": True,
@@ -224,7 +399,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "IQ2_K routed MoE decode, T=1, top-6 of 256 experts, gate/up [2048,4096] "
                                "(fused) + down [4096,2048], bf16 activations",
-                   "experts": E, "top_k": k, "tokens": T, "hidden": H, "intermediate": I,
+                   "experts": E, "top_k": K, "tokens": T, "hidden": H, "intermediate": I,
                    "bytes_per_step": int(bytes_per_step), "weight_pools": POOLS, "graph_steps": S},
         "fraction_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(T / (ms_step * 1e-3), 1),
@@ -235,9 +410,9 @@ def main():
         "ratio_to_own_floor": round(ms_gu / ms_floor, 4),
         "floor_us_per_launch": round(ms_floor * 1e3, 3),
         "stream_read_us_same_bytes": round(ms_stream * 1e3, 3),
-        "floor_rate_vs_stream": round(ms_stream / ms_floor, 4),
         "validation_worst_err": worst,
         "setup_s": round(setup_s, 1),
+        "cells": cells,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
