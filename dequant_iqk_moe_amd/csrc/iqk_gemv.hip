@@ -51,6 +51,10 @@ namespace {
 #define IQK_GEMV_MAX_WAVES 16        // waves per workgroup (launch bound)
 #endif
 constexpr int kMaxWaves = IQK_GEMV_MAX_WAVES;
+// pairs one workgroup may span (the launch plan keeps every block within it);
+// each spanned activation row has its own fixed-point copy in LDS
+constexpr int kMaxSpan = 4;
+static_assert(kMaxSpan == 4, "expert_of selects among four ids");
 
 struct GemvParams {
     const uint8_t* S;
@@ -64,8 +68,9 @@ struct GemvParams {
     const int32_t* ids;
     float* y;
     uint32_t* sink;
-    int32_t nrb;     // row blocks per pair
-    int32_t groups;  // reduction groups per wave
+    int32_t pairs;    // T * k
+    int32_t gpp;      // reduction groups per pair (ceil(out / rows per group))
+    int32_t nblocks;  // workgroups; block b owns groups [b*G/nblocks, (b+1)*G/nblocks)
 };
 
 template <int N>
@@ -435,10 +440,24 @@ __device__ __forceinline__ void load_group(Group<FMT, N>& g, const GemvParams& p
     }
 }
 
+// Position of one reduction group: its pair and its first row in the pair.
+// Groups of a wave are visited in increasing order, nwaves apart, so the
+// cursor advances without a division.
+struct Cursor {
+    int pair, rem;
+    __device__ __forceinline__ void advance(int step, int gpp) {
+        rem += step;
+        while (rem >= gpp) {
+            rem -= gpp;
+            ++pair;
+        }
+    }
+};
+
 template <int FMT, int N, int XDT, bool FLOOR>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
     using G = Geo<N>;
-    __shared__ XLds<N> X;
+    __shared__ XLds<N> X[kMaxSpan];
     __shared__ uint2 grid_s[FMT == IQK_IQ1_S_R4 ? 2048 : 1];
 
     const int nthreads = blockDim.x;
@@ -447,38 +466,38 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nwaves = nthreads >> 6;
     const int bid = blockIdx.x;
-    const int pair = bid / p.nrb;
-    const int rb = bid - pair * p.nrb;
-    const int t = pair / p.k;
-    const int j = pair - t * p.k;
-    const int e = p.ids[pair];
-    // even split of the pair's rows over its row blocks
-    const int row_begin = (int)(((int64_t)rb * p.out) / p.nrb);
-    const int row_end = (int)(((int64_t)(rb + 1) * p.out) / p.nrb);
-    const int64_t out_base = (int64_t)pair * p.out;
-
-    if (e < 0 || e >= p.E) {  // invalid id: NaN rows (all-ones in the floor variant)
-        for (int r = row_begin + tid; r < row_end; r += nthreads) {
-            if constexpr (FLOOR) p.sink[out_base + r] = 0xFFFFFFFFu;
-            else p.y[out_base + r] = __builtin_nanf("");
-        }
-        return;
-    }
+    // The call's rows, pair after pair, are cut into reduction groups that
+    // never straddle a pair; block b takes an equal share of the groups, so
+    // every CU gets the same number of rows whatever T * k is.
+    const int total = p.pairs * p.gpp;
+    const int g0 = (int)(((int64_t)bid * total) / p.nblocks);
+    const int g1 = (int)(((int64_t)(bid + 1) * total) / p.nblocks);
+    const int p_first = g0 / p.gpp;
+    const int p_last = (g1 - 1) / p.gpp;
+    // activation row of a pair: x[t] when shared by the k slots, else x[t, j]
+    auto xrow_of = [&](int pair) { return p.x_slots == 1 ? pair / p.k : pair; };
+    const int xr0 = xrow_of(p_first);
+    const int nx = xrow_of(p_last) - xr0 + 1;
+    int ev[kMaxSpan];
+#pragma unroll
+    for (int i = 0; i < kMaxSpan; ++i) ev[i] = p.ids[min(p_first + i, p_last)];
+    auto expert_of = [&](int pair) {
+        const int d = pair - p_first;
+        return d == 0 ? ev[0] : (d == 1 ? ev[1] : (d == 2 ? ev[2] : ev[3]));
+    };
 
     const int c = lane % G::LPR;  // chunk of k owned by this lane
     const int lane_row = lane / G::LPR;
-    const int64_t e_rows = (int64_t)e * p.out;
-    // Reduction groups of the block are dealt round-robin to the waves, so
-    // the four SIMDs (waves w, w+4, ...) get equal shares of the work.
-    const int nblk_groups = (row_end - row_begin + G::RPG - 1) / G::RPG;
-    auto grp_row = [&](int i) { return row_begin + (wave + i * nwaves) * G::RPG; };
-    const int my_groups = wave < nblk_groups ? (nblk_groups - wave + nwaves - 1) / nwaves : 0;
 
     // the activation is on the critical path: request it first
-    const int64_t xoff = ((int64_t)t * p.x_slots + (p.x_slots == 1 ? 0 : j)) * N;
-    const void* xrow = XDT == IQK_BF16 ? (const void*)((const uint16_t*)p.x + xoff) : (const void*)((const float*)p.x + xoff);
-
-    for (int b = tid; b < N / 16; b += nthreads) prep_block<FMT, N, XDT>(load_xblock<N, XDT>(xrow, b), X, b);
+    for (int i = tid; i < nx * (N / 16); i += nthreads) {
+        const int xi = i / (N / 16);
+        const int b = i - xi * (N / 16);
+        const int64_t xoff = (int64_t)(xr0 + xi) * N;
+        const void* xrow = XDT == IQK_BF16 ? (const void*)((const uint16_t*)p.x + xoff)
+                                           : (const void*)((const float*)p.x + xoff);
+        prep_block<FMT, N, XDT>(load_xblock<N, XDT>(xrow, b), X[xi], b);
+    }
     if constexpr (FMT == IQK_IQ1_S_R4) {
         const uint4* src = (const uint4*)p.grid;
         uint4* dst = (uint4*)grid_s;
@@ -486,28 +505,63 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
     }
     lds_barrier();
 
-    uint32_t xh[16], xl[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint4 a = *(const uint4*)&X.hi[16 * c + 4 * i];
-        const uint4 b = *(const uint4*)&X.lo[16 * c + 4 * i];
-        xh[4 * i] = a.x; xh[4 * i + 1] = a.y; xh[4 * i + 2] = a.z; xh[4 * i + 3] = a.w;
-        xl[4 * i] = b.x; xl[4 * i + 1] = b.y; xl[4 * i + 2] = b.z; xl[4 * i + 3] = b.w;
-    }
-    // The first two groups of rows are requested only now: issued earlier, the
-    // whole launch's row traffic would queue ahead of the activation reads and
-    // hold every wave at the barrier until most rows had streamed in.
-    Group<FMT, N> bufA, bufB;
-    if (my_groups > 0) load_group<FMT, N>(bufA, p, e_rows, grp_row(0), row_end, lane_row, c);
-    if (my_groups > 1) load_group<FMT, N>(bufB, p, e_rows, grp_row(1), row_end, lane_row, c);
-    const float lane_scale = X.scale[c] * p.tab_scale;
-    int32_t bsum[2] = {0, 0};
-    if constexpr (FMT == IQK_IQ1_S_R4) {
-        bsum[0] = X.bsum[2 * c];
-        bsum[1] = X.bsum[2 * c + 1];
-    }
+    const int ngroups = g1 - g0;
+    const int my_groups = wave < ngroups ? (ngroups - wave + nwaves - 1) / nwaves : 0;
+    if (my_groups == 0) return;
+    Cursor lc;  // next group to load
+    lc.pair = (g0 + wave) / p.gpp;
+    lc.rem = g0 + wave - lc.pair * p.gpp;
+    Cursor pc = lc;  // next group to process
 
-    auto process = [&](const Group<FMT, N>& gb, int grp_row0) {
+    auto load_next = [&](Group<FMT, N>& buf) {
+        const int e = expert_of(lc.pair);
+        if ((unsigned)e < (unsigned)p.E)
+            load_group<FMT, N>(buf, p, (int64_t)e * p.out, lc.rem * G::RPG, p.out, lane_row, c);
+        lc.advance(nwaves, p.gpp);
+    };
+    // The first two groups of rows are requested only after the activation:
+    // issued earlier, the launch's row traffic would queue ahead of the
+    // activation reads and hold every wave at the barrier.
+    Group<FMT, N> bufA, bufB;
+    load_next(bufA);
+    if (my_groups > 1) load_next(bufB);
+
+    uint32_t xh[16], xl[16];
+    float lane_scale = 0.f;
+    int32_t bsum[2] = {0, 0};
+    int cur_x = -1;
+    auto load_x = [&](int xi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 a = *(const uint4*)&X[xi].hi[16 * c + 4 * i];
+            const uint4 b = *(const uint4*)&X[xi].lo[16 * c + 4 * i];
+            xh[4 * i] = a.x; xh[4 * i + 1] = a.y; xh[4 * i + 2] = a.z; xh[4 * i + 3] = a.w;
+            xl[4 * i] = b.x; xl[4 * i + 1] = b.y; xl[4 * i + 2] = b.z; xl[4 * i + 3] = b.w;
+        }
+        lane_scale = X[xi].scale[c] * p.tab_scale;
+        if constexpr (FMT == IQK_IQ1_S_R4) {
+            bsum[0] = X[xi].bsum[2 * c];
+            bsum[1] = X[xi].bsum[2 * c + 1];
+        }
+        cur_x = xi;
+    };
+
+    auto process = [&](const Group<FMT, N>& gb) {
+        const int pair = pc.pair;
+        const int grp_row0 = pc.rem * G::RPG;
+        pc.advance(nwaves, p.gpp);
+        const int64_t out_base = (int64_t)pair * p.out;
+        const int e = expert_of(pair);
+        if ((unsigned)e >= (unsigned)p.E) {  // invalid id: NaN rows (all-ones in the floor variant)
+            const int r = grp_row0 + lane;
+            if (lane < G::RPG && r < p.out) {
+                if constexpr (FLOOR) p.sink[out_base + r] = 0xFFFFFFFFu;
+                else p.y[out_base + r] = __builtin_nanf("");
+            }
+            return;
+        }
+        const int xi = xrow_of(pair) - xr0;
+        if (xi != cur_x) load_x(xi);
         uint32_t part[G::GIT];
 #pragma unroll
         for (int it = 0; it < G::GIT; ++it) {
@@ -523,41 +577,44 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
         bool writer;
         const uint32_t sum = reduce_group<N, FLOOR>(part, lane, &row_in_grp, &writer);
         const int r = grp_row0 + row_in_grp;
-        if (writer && r < row_end) {
+        if (writer && r < p.out) {
             if constexpr (FLOOR) p.sink[out_base + r] = sum;
             else p.y[out_base + r] = __uint_as_float(sum);
         }
     };
 
     for (int i = 0; i < my_groups; i += 2) {
-        process(bufA, grp_row(i));
-        if (i + 2 < my_groups) load_group<FMT, N>(bufA, p, e_rows, grp_row(i + 2), row_end, lane_row, c);
+        process(bufA);
+        if (i + 2 < my_groups) load_next(bufA);
         if (i + 1 >= my_groups) break;
-        process(bufB, grp_row(i + 1));
-        if (i + 3 < my_groups) load_group<FMT, N>(bufB, p, e_rows, grp_row(i + 3), row_end, lane_row, c);
+        process(bufB);
+        if (i + 3 < my_groups) load_next(bufB);
     }
 }
 
 template <int FMT, int N, int XDT, bool FLOOR>
 hipError_t launch_inst(GemvParams p, int64_t pairs, hipStream_t s) {
     using G = Geo<N>;
-    // one large workgroup per CU over the whole call: split each pair's rows
-    // into nrb blocks with pairs * nrb <= 256, each block a few row groups per wave
-    int64_t nrb = IQK_GEMV_TARGET_BLOCKS / (pairs > 0 ? pairs : 1);
-    const int64_t max_nrb = (p.out + G::RPG - 1) / G::RPG;
-    nrb = nrb < 1 ? 1 : (nrb > max_nrb ? max_nrb : nrb);
-    const int64_t rows = (p.out + nrb - 1) / nrb;           // rows of the largest block
-    const int64_t groups = (rows + G::RPG - 1) / G::RPG;    // reduction groups per block
+    // one large workgroup per CU over the whole call; more blocks only when
+    // a block would otherwise span more than kMaxSpan pairs (small out)
+    const int64_t gpp = (p.out + G::RPG - 1) / G::RPG;
+    const int64_t total = pairs * gpp;
+    if (total <= 0 || total > 0x7FFFFFFF) return hipErrorInvalidValue;
+    int64_t nb = total < IQK_GEMV_TARGET_BLOCKS ? total : IQK_GEMV_TARGET_BLOCKS;
+    // a block of at most (kMaxSpan - 1) * gpp + 1 groups touches at most kMaxSpan pairs
+    const int64_t span_groups = (kMaxSpan - 1) * gpp + 1;
+    const int64_t nb_span = (total + span_groups - 1) / span_groups;
+    nb = nb < nb_span ? nb_span : nb;
+    const int64_t groups = (total + nb - 1) / nb;  // reduction groups of the largest block
     // waves: a multiple of four (one share per SIMD) up to 16, at least
     // IQK_GEMV_MIN_GROUPS groups each once the block is large enough
     int64_t waves = (groups + IQK_GEMV_MIN_GROUPS - 1) / IQK_GEMV_MIN_GROUPS;
     waves = groups < 4 ? groups : ((waves + 3) / 4) * 4;
     waves = waves > kMaxWaves ? kMaxWaves : (waves < 1 ? 1 : waves);
-    p.nrb = (int32_t)nrb;
-    p.groups = 0;
-    const int64_t blocks = pairs * nrb;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gemv_kernel<FMT, N, XDT, FLOOR>), dim3((unsigned)blocks), dim3((unsigned)(64 * waves)), 0, s, p);
+    p.pairs = (int32_t)pairs;
+    p.gpp = (int32_t)gpp;
+    p.nblocks = (int32_t)nb;
+    hipLaunchKernelGGL((gemv_kernel<FMT, N, XDT, FLOOR>), dim3((unsigned)nb), dim3((unsigned)(64 * waves)), 0, s, p);
     return hipGetLastError();
 }
 
@@ -603,7 +660,7 @@ hipError_t launch_gemv(const GemvLaunch& a, bool floor_variant, hipStream_t s) {
     p.ids = a.ids;
     p.y = a.y;
     p.sink = a.sink;
-    p.nrb = p.groups = 0;
+    p.pairs = p.gpp = p.nblocks = 0;
     const int64_t pairs = a.T * a.k;
     return floor_variant ? launch_fmt<true>(p, a.fmt, a.n, a.x_dtype, pairs, s)
                          : launch_fmt<false>(p, a.fmt, a.n, a.x_dtype, pairs, s);

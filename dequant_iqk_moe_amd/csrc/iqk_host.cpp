@@ -271,6 +271,9 @@ int check_gemv_args(const iqk_weights* w, const float* values, const int8_t* gri
     if (T < 0 || k <= 0) return fail(IQK_E_ARG, "T must be >= 0 and k > 0");
     if (T * k > 65535LL * 64) return fail(IQK_E_ARG, "T*k = %lld exceeds the decode limit", (long long)(T * k));
     if (x_slots != 1 && x_slots != k) return fail(IQK_E_ARG, "x_slots must be 1 or k");
+    // the kernel indexes 4-row reduction groups of the whole call in 32 bits
+    if (T * k * ((w->out + 3) / 4) > 0x7FFFFFFFLL)
+        return fail(IQK_E_ARG, "T*k*ceil(out/4) = %lld exceeds 2^31 - 1", (long long)(T * k * ((w->out + 3) / 4)));
     if (x_dtype != IQK_F32 && x_dtype != IQK_BF16) return fail(IQK_E_ARG, "x_dtype must be IQK_F32 or IQK_BF16");
     if (T > 0 && (!x || !ids || !y)) return fail(IQK_E_ARG, "null x, ids or output");
     L->fmt = w->fmt;

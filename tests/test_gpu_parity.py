@@ -103,6 +103,9 @@ def _gemv_case(fmt, n, out, T, k, E, x_dtype, x_slots, seed):
     (2048, 72, 3, 4, 8, 4),     # per-pair input (down)
     (512, 72, 2, 3, 5, 1),
     (2048, 4100, 1, 2, 3, 1),   # several groups per wave, ragged tail of 4 rows
+    (512, 8, 300, 6, 40, 6),    # blocks span four pairs, four activation rows each
+    (4096, 12, 50, 6, 20, 1),   # blocks span pairs of two tokens
+    (2048, 6, 40, 5, 10, 5),    # two-row groups per pair, ragged, per-pair input
 ])
 def test_gemv_parity(fmt, n, out, T, k, E, x_slots, x_dtype):
     announce(f"gemv fmt={fmt} n={n} out={out} T={T} k={k} E={E} slots={x_slots} x={x_dtype}")
@@ -162,6 +165,24 @@ def test_gemv_invalid_ids_give_nan_rows():
     assert np.all(np.isnan(y[0, 1])) and np.all(np.isnan(y[0, 2]))
     ref = oracle.moe(fmt, s, E, out, n, x, ids, values)
     assert np.all(rel_err_per_vector(y[0, [0, 3]], ref[0, [0, 3]]) <= TOL_GEMV)
+
+
+def test_gemv_invalid_ids_inside_multi_pair_blocks():
+    # out = 8 rows at n = 512 is one reduction group per pair, so every
+    # workgroup spans several pairs; invalid ids must only blank their own
+    fmt, n, out, E, T, k = K, 512, 8, 12, 64, 6
+    _, w, s = _weights(fmt, E, out, n, 510)
+    values = synth.values_table(511)
+    ids = synth.topk_ids(T, k, E, 512)
+    rng = np.random.default_rng(513)
+    bad = rng.random(ids.shape) < 0.15
+    ids = np.where(bad, np.where(rng.random(ids.shape) < 0.5, -3, E + 4), ids).astype(np.int32)
+    x = bf16_round(synth.normal((T, k, n), 514))
+    announce("gemv invalid ids in multi-pair blocks")
+    y = q.moe_gemv(w, to_dev(x, torch.bfloat16), to_dev(ids), values, x_slots=k).cpu().numpy()
+    assert np.all(np.isnan(y[bad]))
+    ref = oracle.moe(fmt, s, E, out, n, x, ids, values, x_slots=k)
+    assert np.all(rel_err_per_vector(y[~bad], ref[~bad]) <= TOL_GEMV)
 
 
 def test_gemv_activation_outliers_and_zeros():
