@@ -56,6 +56,34 @@ constexpr int kMaxWaves = IQK_GEMV_MAX_WAVES;
 constexpr int kMaxSpan = 4;
 static_assert(kMaxSpan == 4, "expert_of selects among four ids");
 
+// Unsigned division by a launch constant d >= 1 without a division sequence
+// (the scalar unit has no divide; the compiler's expansion is ~40
+// instructions on the kernel's critical path).  Round-up method: with
+// l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1 and t = mulhi(n, m),
+// n / d = (t + ((n - t) >> 1)) >> (l - 1) for every 32-bit n and d >= 2
+// (T. Granlund and P. L. Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994); d = 1 is passed through.
+struct FastDiv {
+    uint32_t m, s, d;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f{0u, 0u, d};
+    if (d > 1) {
+        uint32_t l = 0;
+        while ((1ull << l) < d) ++l;
+        f.m = (uint32_t)((((1ull << 32) * ((1ull << l) - d)) / d) + 1);
+        f.s = l - 1;
+    }
+    return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+    if (f.d == 1) return n;
+    const uint32_t t = __umulhi(n, f.m);
+    return (t + ((n - t) >> 1)) >> f.s;
+}
+
 struct GemvParams {
     const uint8_t* S;
     int64_t off0, off1, off2, off3, off4;
@@ -70,7 +98,9 @@ struct GemvParams {
     uint32_t* sink;
     int32_t pairs;    // T * k
     int32_t gpp;      // reduction groups per pair (ceil(out / rows per group))
-    int32_t nblocks;  // workgroups; block b owns groups [b*G/nblocks, (b+1)*G/nblocks)
+    int32_t gbase;    // groups per block: gbase, plus one for the first grem blocks
+    int32_t grem;
+    FastDiv dgpp, dk; // division by gpp and by k
 };
 
 template <int N>
@@ -469,13 +499,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
     // The call's rows, pair after pair, are cut into reduction groups that
     // never straddle a pair; block b takes an equal share of the groups, so
     // every CU gets the same number of rows whatever T * k is.
-    const int total = p.pairs * p.gpp;
-    const int g0 = (int)(((int64_t)bid * total) / p.nblocks);
-    const int g1 = (int)(((int64_t)(bid + 1) * total) / p.nblocks);
-    const int p_first = g0 / p.gpp;
-    const int p_last = (g1 - 1) / p.gpp;
+    const int g0 = bid * p.gbase + min(bid, p.grem);
+    const int g1 = g0 + p.gbase + (bid < p.grem ? 1 : 0);
+    const int p_first = (int)fdiv((uint32_t)g0, p.dgpp);
+    const int p_last = (int)fdiv((uint32_t)(g1 - 1), p.dgpp);
     // activation row of a pair: x[t] when shared by the k slots, else x[t, j]
-    auto xrow_of = [&](int pair) { return p.x_slots == 1 ? pair / p.k : pair; };
+    auto xrow_of = [&](int pair) { return p.x_slots == 1 ? (int)fdiv((uint32_t)pair, p.dk) : pair; };
     const int xr0 = xrow_of(p_first);
     const int nx = xrow_of(p_last) - xr0 + 1;
     int ev[kMaxSpan];
@@ -489,19 +518,29 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
     const int c = lane % G::LPR;  // chunk of k owned by this lane
     const int lane_row = lane / G::LPR;
 
-    // the activation is on the critical path: request it first
-    for (int i = tid; i < nx * (N / 16); i += nthreads) {
-        const int xi = i / (N / 16);
-        const int b = i - xi * (N / 16);
-        const int64_t xoff = (int64_t)(xr0 + xi) * N;
-        const void* xrow = XDT == IQK_BF16 ? (const void*)((const uint16_t*)p.x + xoff)
-                                           : (const void*)((const float*)p.x + xoff);
-        prep_block<FMT, N, XDT>(load_xblock<N, XDT>(xrow, b), X[xi], b);
-    }
+    // The activation (and the IQ1_S_R4 grid) is on the critical path: every
+    // first-pass load is issued before any of them is waited for.
+    auto xrow_ptr = [&](int i) {
+        const int64_t xoff = (int64_t)(xr0 + i / (N / 16)) * N;
+        return XDT == IQK_BF16 ? (const void*)((const uint16_t*)p.x + xoff) : (const void*)((const float*)p.x + xoff);
+    };
+    const int xtotal = nx * (N / 16);
+    XRaw<XDT> xraw;
+    if (tid < xtotal) xraw = load_xblock<N, XDT>(xrow_ptr(tid), tid % (N / 16));
+    uint4 gw0, gw1;
+    const uint4* gsrc = (const uint4*)p.grid;
+    uint4* gdst = (uint4*)grid_s;
     if constexpr (FMT == IQK_IQ1_S_R4) {
-        const uint4* src = (const uint4*)p.grid;
-        uint4* dst = (uint4*)grid_s;
-        for (int i = tid; i < 1024; i += nthreads) dst[i] = src[i];
+        if (tid < 1024) gw0 = gsrc[tid];
+        if (tid + nthreads < 1024) gw1 = gsrc[tid + nthreads];
+    }
+    if (tid < xtotal) prep_block<FMT, N, XDT>(xraw, X[tid / (N / 16)], tid % (N / 16));
+    for (int i = tid + nthreads; i < xtotal; i += nthreads)
+        prep_block<FMT, N, XDT>(load_xblock<N, XDT>(xrow_ptr(i), i % (N / 16)), X[i / (N / 16)], i % (N / 16));
+    if constexpr (FMT == IQK_IQ1_S_R4) {
+        if (tid < 1024) gdst[tid] = gw0;
+        if (tid + nthreads < 1024) gdst[tid + nthreads] = gw1;
+        for (int i = tid + 2 * nthreads; i < 1024; i += nthreads) gdst[i] = gsrc[i];
     }
     lds_barrier();
 
@@ -509,7 +548,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
     const int my_groups = wave < ngroups ? (ngroups - wave + nwaves - 1) / nwaves : 0;
     if (my_groups == 0) return;
     Cursor lc;  // next group to load
-    lc.pair = (g0 + wave) / p.gpp;
+    lc.pair = (int)fdiv((uint32_t)(g0 + wave), p.dgpp);
     lc.rem = g0 + wave - lc.pair * p.gpp;
     Cursor pc = lc;  // next group to process
 
@@ -613,7 +652,10 @@ hipError_t launch_inst(GemvParams p, int64_t pairs, hipStream_t s) {
     waves = waves > kMaxWaves ? kMaxWaves : (waves < 1 ? 1 : waves);
     p.pairs = (int32_t)pairs;
     p.gpp = (int32_t)gpp;
-    p.nblocks = (int32_t)nb;
+    p.gbase = (int32_t)(total / nb);
+    p.grem = (int32_t)(total % nb);
+    p.dgpp = make_fastdiv((uint32_t)gpp);
+    p.dk = make_fastdiv((uint32_t)p.k);
     hipLaunchKernelGGL((gemv_kernel<FMT, N, XDT, FLOOR>), dim3((unsigned)nb), dim3((unsigned)(64 * waves)), 0, s, p);
     return hipGetLastError();
 }
@@ -660,7 +702,7 @@ hipError_t launch_gemv(const GemvLaunch& a, bool floor_variant, hipStream_t s) {
     p.ids = a.ids;
     p.y = a.y;
     p.sink = a.sink;
-    p.pairs = p.gpp = p.nblocks = 0;
+    p.pairs = p.gpp = p.gbase = p.grem = 0;
     const int64_t pairs = a.T * a.k;
     return floor_variant ? launch_fmt<true>(p, a.fmt, a.n, a.x_dtype, pairs, s)
                          : launch_fmt<false>(p, a.fmt, a.n, a.x_dtype, pairs, s);
