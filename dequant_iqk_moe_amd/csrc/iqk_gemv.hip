@@ -121,6 +121,33 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Raw buffer resources.  An access at or past a resource's record count
+// reads zero and a store there is dropped, so every row load and result
+// store below is issued by every lane in every case: work that is absent (a
+// row past the end, a group past the wave's last, an invalid expert id) gets
+// an out-of-range offset or a resource of zero records instead of a branch.
+// With no memory operation behind a branch the compiler counts outstanding
+// loads exactly, and a wave waits for one group of rows while the next group
+// stays in flight.
+using Rsrc = __amdgpu_buffer_rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw (unswizzled) buffer, 32-bit data format
+constexpr uint32_t kOob = 0x80000000u;  // an offset past every resource used here
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ uint4 ld128(Rsrc r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint2 ld64(Rsrc r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ uint32_t ld32(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+__device__ __forceinline__ uint32_t ld16(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0); }
+__device__ __forceinline__ uint32_t ld8(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0); }
+
 __device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) { return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false); }
 __device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) { return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false); }
 __device__ __forceinline__ uint32_t dpp_half_mirror(uint32_t v) { return __builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, false); }
@@ -295,46 +322,62 @@ struct Strides {
     static constexpr int P4 = FMT == IQK_IQ2_KS ? 2 : 0;
 };
 
-// Load the words of one lane for the row `grow0 + dl` (grow0 uniform, dl the
-// lane's non-negative row offset inside the iteration).  Plane base pointers
-// are uniform and lane offsets unsigned 32-bit, so every load is the
-// scalar-base + vector-offset form.
+// Plane resources of one expert's rows; zero records for an invalid id, so
+// its loads read zeros and move no data.
+struct ExpertRes {
+    Rsrc q, a, b, c, d;
+};
+
 template <int FMT, int N>
-__device__ __forceinline__ RowData load_row(const GemvParams& p, int64_t grow0, uint32_t dl, uint32_t c) {
+__device__ __forceinline__ ExpertRes expert_res(const GemvParams& p, int e) {
+    using St = Strides<FMT, N>;
+    const bool valid = (unsigned)e < (unsigned)p.E;
+    const int64_t row0 = (int64_t)(valid ? e : 0) * p.out;
+    const uint32_t rows = valid ? (uint32_t)p.out : 0u;
+    const uint8_t* S = p.S;
+    ExpertRes r;
+    r.q = make_rsrc(S + p.off0 + row0 * St::QS, rows * St::QS);
+    r.a = make_rsrc(S + p.off1 + row0 * St::P1, rows * St::P1);
+    if constexpr (FMT == IQK_IQ2_K) {
+        r.b = make_rsrc(S + p.off2 + row0 * St::P2, rows * St::P2);
+        r.d = make_rsrc(S + p.off3 + row0 * St::P3, rows * St::P3);
+        r.c = r.b;
+    } else if constexpr (FMT == IQK_IQ2_KS) {
+        r.b = make_rsrc(S + p.off2 + row0 * St::P2, rows * St::P2);
+        r.c = make_rsrc(S + p.off3 + row0 * St::P3, rows * St::P3);
+        r.d = make_rsrc(S + p.off4 + row0 * 2, rows * 2u);
+    } else {
+        r.d = make_rsrc(S + p.off2 + row0 * 2, rows * 2u);
+        r.b = r.c = r.d;
+    }
+    return r;
+}
+
+// The words one lane needs for expert row `row` (rows at or past `out` are
+// out of range and read zeros).  Resources are uniform, offsets per lane.
+template <int FMT, int N>
+__device__ __forceinline__ RowData load_row(const ExpertRes& x, uint32_t row, uint32_t c) {
     using St = Strides<FMT, N>;
     RowData r;
-    const uint8_t* S = p.S;
     if constexpr (FMT == IQK_IQ2_K) {
-        const uint8_t* b0 = S + p.off0 + grow0 * St::QS;
-        const uint8_t* b1 = S + p.off1 + grow0 * St::P1;
-        const uint8_t* b2 = S + p.off2 + grow0 * St::P2;
-        const uint8_t* b3 = S + p.off3 + grow0 * St::P3;
-        r.q = *(const uint4*)(b0 + (dl * (uint32_t)St::QS + 16u * c));
-        r.a = *(const uint16_t*)(b1 + (dl * (uint32_t)St::P1 + 2u * c));
-        r.b = b2[dl * (uint32_t)St::P2 + (c >> 1)];
+        r.q = ld128(x.q, row * St::QS + 16u * c);
+        r.a = ld16(x.a, row * St::P1 + 2u * c);
+        r.b = ld8(x.b, row * St::P2 + (c >> 1));
         r.c = 0;
-        r.d = *(const uint16_t*)(b3 + (dl * (uint32_t)St::P3 + 2u * (c >> 2)));
+        r.d = ld16(x.d, row * St::P3 + 2u * (c >> 2));
     } else if constexpr (FMT == IQK_IQ2_KS) {
-        const uint8_t* b0 = S + p.off0 + grow0 * St::QS;
-        const uint8_t* b1 = S + p.off1 + grow0 * St::P1;
-        const uint8_t* b2 = S + p.off2 + grow0 * St::P2;
-        const uint8_t* b3 = S + p.off3 + grow0 * St::P3;
-        const uint8_t* b4 = S + p.off4 + grow0 * 2;
-        r.q = *(const uint4*)(b0 + (dl * (uint32_t)St::QS + 16u * c));
-        r.a = b1[dl * (uint32_t)St::P1 + c];
-        r.b = b2[dl * (uint32_t)St::P2 + (c >> 2)];
-        r.c = b3[dl * (uint32_t)St::P3 + (c >> 2)];
-        r.d = *(const uint16_t*)(b4 + 2u * dl);
+        r.q = ld128(x.q, row * St::QS + 16u * c);
+        r.a = ld8(x.a, row * St::P1 + c);
+        r.b = ld8(x.b, row * St::P2 + (c >> 2));
+        r.c = ld8(x.c, row * St::P3 + (c >> 2));
+        r.d = ld16(x.d, row * 2u);
     } else {
-        const uint8_t* b0 = S + p.off0 + grow0 * St::QS;
-        const uint8_t* b1 = S + p.off1 + grow0 * St::P1;
-        const uint8_t* b2 = S + p.off2 + grow0 * 2;
-        const uint2 qq = *(const uint2*)(b0 + (dl * (uint32_t)St::QS + 8u * c));
+        const uint2 qq = ld64(x.q, row * St::QS + 8u * c);
         r.q = make_uint4(qq.x, qq.y, 0, 0);
-        r.a = *(const uint32_t*)(b1 + (dl * (uint32_t)St::P1 + 4u * c));
+        r.a = ld32(x.a, row * St::P1 + 4u * c);
         r.b = 0;
         r.c = 0;
-        r.d = *(const uint16_t*)(b2 + 2u * dl);
+        r.d = ld16(x.d, row * 2u);
     }
     return r;
 }
@@ -456,18 +499,11 @@ struct Group {
 };
 
 template <int FMT, int N>
-__device__ __forceinline__ void load_group(Group<FMT, N>& g, const GemvParams& p, int64_t e_rows, int grp_row0,
-                                           int row_end, int lane_row, int c) {
+__device__ __forceinline__ void load_group(Group<FMT, N>& g, const ExpertRes& res, int grp_row0, int lane_row, int c) {
     using G = Geo<N>;
 #pragma unroll
-    for (int it = 0; it < G::GIT; ++it) {
-        // uniform first row of the iteration, clamped into the block; rows past
-        // the end re-read the last row and are not written
-        const int r0 = min(grp_row0 + it * G::RPI, row_end - 1);
-        uint32_t dl = 0;
-        if constexpr (G::LPR != 64) dl = (uint32_t)min(lane_row, row_end - 1 - r0);
-        g.r[it] = load_row<FMT, N>(p, e_rows + r0, dl, (uint32_t)c);
-    }
+    for (int it = 0; it < G::GIT; ++it)
+        g.r[it] = load_row<FMT, N>(res, (uint32_t)(grp_row0 + it * G::RPI + lane_row), (uint32_t)c);
 }
 
 // Position of one reduction group: its pair and its first row in the pair.
@@ -552,18 +588,18 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
     lc.rem = g0 + wave - lc.pair * p.gpp;
     Cursor pc = lc;  // next group to process
 
-    auto load_next = [&](Group<FMT, N>& buf) {
-        const int e = expert_of(lc.pair);
-        if ((unsigned)e < (unsigned)p.E)
-            load_group<FMT, N>(buf, p, (int64_t)e * p.out, lc.rem * G::RPG, p.out, lane_row, c);
+    // Loads of a group past the wave's last use a zero-record resource.
+    auto load_next = [&](Group<FMT, N>& buf, bool live) {
+        const ExpertRes res = expert_res<FMT, N>(p, live ? expert_of(lc.pair) : -1);
+        load_group<FMT, N>(buf, res, lc.rem * G::RPG, lane_row, c);
         lc.advance(nwaves, p.gpp);
     };
-    // The first two groups of rows are requested only after the activation:
-    // issued earlier, the launch's row traffic would queue ahead of the
-    // activation reads and hold every wave at the barrier.
+    // The first two groups of rows are requested only now: issued earlier, the
+    // launch's row traffic would queue ahead of the activation reads and
+    // hold every wave at the barrier until most rows had streamed in.
     Group<FMT, N> bufA, bufB;
-    load_next(bufA);
-    if (my_groups > 1) load_next(bufB);
+    load_next(bufA, true);
+    load_next(bufB, my_groups > 1);
 
     uint32_t xh[16], xl[16];
     float lane_scale = 0.f;
@@ -589,16 +625,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
         const int pair = pc.pair;
         const int grp_row0 = pc.rem * G::RPG;
         pc.advance(nwaves, p.gpp);
-        const int64_t out_base = (int64_t)pair * p.out;
-        const int e = expert_of(pair);
-        if ((unsigned)e >= (unsigned)p.E) {  // invalid id: NaN rows (all-ones in the floor variant)
-            const int r = grp_row0 + lane;
-            if (lane < G::RPG && r < p.out) {
-                if constexpr (FLOOR) p.sink[out_base + r] = 0xFFFFFFFFu;
-                else p.y[out_base + r] = __builtin_nanf("");
-            }
-            return;
-        }
+        const bool valid = (unsigned)expert_of(pair) < (unsigned)p.E;
         const int xi = xrow_of(pair) - xr0;
         if (xi != cur_x) load_x(xi);
         uint32_t part[G::GIT];
@@ -614,20 +641,35 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
         }
         int row_in_grp;
         bool writer;
-        const uint32_t sum = reduce_group<N, FLOOR>(part, lane, &row_in_grp, &writer);
+        uint32_t sum = reduce_group<N, FLOOR>(part, lane, &row_in_grp, &writer);
+        // invalid id: its rows read zeros; they are reported as NaN (all ones
+        // in the floor variant)
+        if (!valid) sum = FLOOR ? 0xFFFFFFFFu : 0x7FC00000u;
         const int r = grp_row0 + row_in_grp;
-        if (writer && r < p.out) {
-            if constexpr (FLOOR) p.sink[out_base + r] = sum;
-            else p.y[out_base + r] = __uint_as_float(sum);
-        }
+        void* ybase = FLOOR ? (void*)(p.sink + (int64_t)pair * p.out) : (void*)(p.y + (int64_t)pair * p.out);
+        const Rsrc yres = make_rsrc(ybase, (uint32_t)p.out * 4u);
+        __builtin_amdgcn_raw_buffer_store_b32(sum, yres, writer ? (uint32_t)r * 4u : kOob, 0, 0);
     };
 
-    for (int i = 0; i < my_groups; i += 2) {
-        process(bufA);
-        if (i + 2 < my_groups) load_next(bufA);
-        if (i + 1 >= my_groups) break;
+    // Groups 0 and 1 are in flight.  The loop refills a buffer just before
+    // processing the other one, so at its top exactly one group's loads are
+    // outstanding on every path and each wait covers only the group it needs.
+    load_x(xrow_of(pc.pair) - xr0);
+    process(bufA);
+    if constexpr (FMT == IQK_IQ1_S_R4) {
+        // measured: at one or two groups per wave the IQ1_S_R4 instance is
+        // faster without the loop's dead refills (the 2-bit ones are not)
+        if (my_groups <= 2) {
+            if (my_groups == 2) process(bufB);
+            return;
+        }
+    }
+    for (int i = 1; i < my_groups; i += 2) {
+        load_next(bufA, i + 1 < my_groups);
         process(bufB);
-        if (i + 3 < my_groups) load_next(bufB);
+        load_next(bufB, i + 2 < my_groups);
+        if (i + 1 >= my_groups) break;
+        process(bufA);
     }
 }
 
