@@ -79,6 +79,8 @@ def _load():
         "iqk_unpack_relayout": (i32, [i32, p, sz, i64, i64, p, sz]),
         "iqk_dequant": (i32, [W, i64, i64, p, p, i32, p, p]),
         "iqk_moe_gemv": (i32, [W, p, p, p, i32, i32, p, i64, i32, p, p]),
+        "iqk_moe_gemv_swiglu": (i32, [W, p, p, p, i32, i32, p, i64, i32, p, p]),
+        "iqk_moe_gemv_combine": (i32, [W, p, p, p, i32, i32, p, p, i64, i32, p, p]),
         "iqk_route": (i32, [p, i64, i64, i32, p, p, p, p]),
         "iqk_grouped_gemm": (i32, [p, i64, i64, i64, p, i32, i64, i32, p, p, p, p]),
         "iqk_moe_prefill_workspace": (i32, [W, i64, i32, p]),
@@ -222,6 +224,40 @@ def moe_gemv(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=None, grid: 
     cw = w._c()
     _check(_lib.iqk_moe_gemv(ctypes.byref(cw), vp, _dev(grid, "grid", torch.int8), xp, xdt, x_slots,
                              _dev(ids, "ids", torch.int32), T, k, _dev(y, "y", torch.float32), _stream(stream)))
+    return y
+
+
+def moe_gemv_swiglu(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=None, grid: torch.Tensor | None = None,
+                    x_slots: int = 1, h: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Gate/up matvec with the SwiGLU epilogue: h[T, k, out // 2] (bf16),
+    h = silu(gate) * up with gate rows [0, I) and up rows [I, 2I)."""
+    T, k = ids.shape
+    xp, xdt = _x_args(x, T, x_slots, w.in_features)
+    if h is None:
+        h = torch.empty((T, k, w.out // 2), dtype=torch.bfloat16, device=w.streams.device)
+    _v, vp = _host_values(values)
+    cw = w._c()
+    _check(_lib.iqk_moe_gemv_swiglu(ctypes.byref(cw), vp, _dev(grid, "grid", torch.int8), xp, xdt, x_slots,
+                                    _dev(ids, "ids", torch.int32), T, k, _dev(h, "h", torch.bfloat16),
+                                    _stream(stream)))
+    return h
+
+
+def moe_gemv_combine(w: Weights, x: torch.Tensor, ids: torch.Tensor, route_w: torch.Tensor, values=None,
+                     grid: torch.Tensor | None = None, x_slots: int | None = None, y: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """Down matvec with the router-weighted combine: y[T, out] (float32),
+    y[t] = sum_j route_w[t, j] * W_{ids[t, j]} x[t, j].  x_slots defaults to k."""
+    T, k = ids.shape
+    x_slots = k if x_slots is None else x_slots
+    xp, xdt = _x_args(x, T, x_slots, w.in_features)
+    if y is None:
+        y = torch.empty((T, w.out), dtype=torch.float32, device=w.streams.device)
+    _v, vp = _host_values(values)
+    cw = w._c()
+    _check(_lib.iqk_moe_gemv_combine(ctypes.byref(cw), vp, _dev(grid, "grid", torch.int8), xp, xdt, x_slots,
+                                     _dev(ids, "ids", torch.int32), _dev(route_w, "route_w", torch.float32), T, k,
+                                     _dev(y, "y", torch.float32), _stream(stream)))
     return y
 
 

@@ -84,6 +84,16 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
     return (t + ((n - t) >> 1)) >> f.s;
 }
 
+// What a launch writes after the row sums (see the entry points):
+//   kPlain   y[t, j, o] (fp32), one unit = one pair's row group;
+//   kSwiGLU  h[t, j, i] = silu(gate_i) * up_i (bf16) from a gate/up tensor
+//            whose rows [0, I) are gate and [I, 2I) up; a unit holds
+//            RPG/2 gate rows and the matching up rows;
+//   kCombine y[t, o] = sum_j w[t, j] * (row o of expert ids[t, j]) . x_j
+//            (fp32); a unit is one token's row group, visited once per slot
+//            j = 0..k-1 in order, accumulated in registers.
+enum GemvMode { kPlain = 0, kSwiGLU = 1, kCombine = 2 };
+
 struct GemvParams {
     const uint8_t* S;
     int64_t off0, off1, off2, off3, off4;
@@ -94,13 +104,16 @@ struct GemvParams {
     const void* x;
     int32_t x_slots, k;
     const int32_t* ids;
-    float* y;
-    uint32_t* sink;
-    int32_t pairs;    // T * k
-    int32_t gpp;      // reduction groups per pair (ceil(out / rows per group))
-    int32_t gbase;    // groups per block: gbase, plus one for the first grem blocks
-    int32_t grem;
-    FastDiv dgpp, dk; // division by gpp and by k
+    float* y;           // kPlain: [T, k, out]; kCombine: [T, out]
+    uint32_t* sink;     // floor variant output
+    uint16_t* h;        // kSwiGLU: bf16 [T, k, out / 2]
+    const float* rw;    // kCombine: router weights [T, k]
+    int32_t outers;     // pairs (kPlain, kSwiGLU) or tokens (kCombine)
+    int32_t upo;        // units per outer
+    int32_t ubase;      // units per block: ubase, plus one for the first urem blocks
+    int32_t urem;       //   (kCombine: per block of one token, bpt blocks per token)
+    int32_t bpt;
+    FastDiv dupo, dk, dbpt;
 };
 
 template <int N>
@@ -498,32 +511,48 @@ struct Group {
     RowData r[Geo<N>::GIT];
 };
 
-template <int FMT, int N>
-__device__ __forceinline__ void load_group(Group<FMT, N>& g, const ExpertRes& res, int grp_row0, int lane_row, int c) {
+// Rows of one unit: local row q = it * RPI + lane_row maps to an expert row
+// through `row_of` (identity plus offset, or the gate/up split).
+template <int FMT, int N, class RowOf>
+__device__ __forceinline__ void load_group(Group<FMT, N>& g, const ExpertRes& res, RowOf row_of, int lane_row, int c) {
     using G = Geo<N>;
 #pragma unroll
     for (int it = 0; it < G::GIT; ++it)
-        g.r[it] = load_row<FMT, N>(res, (uint32_t)(grp_row0 + it * G::RPI + lane_row), (uint32_t)c);
+        g.r[it] = load_row<FMT, N>(res, (uint32_t)row_of(it * G::RPI + lane_row), (uint32_t)c);
 }
 
-// Position of one reduction group: its pair and its first row in the pair.
-// Groups of a wave are visited in increasing order, nwaves apart, so the
-// cursor advances without a division.
+// float -> bf16, round to nearest even (NaN stays a quiet NaN)
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Position of one item: its outer index (pair, or token for kCombine), its
+// unit inside the outer, and the slot j (kCombine).  Items of a wave are
+// visited in increasing order, units nwaves apart, so the cursor advances
+// without a division.
 struct Cursor {
-    int pair, rem;
-    __device__ __forceinline__ void advance(int step, int gpp) {
+    int outer, rem, j;
+    __device__ __forceinline__ void advance(int step, int upo, int kk) {
+        if (++j < kk) return;
+        j = 0;
         rem += step;
-        while (rem >= gpp) {
-            rem -= gpp;
-            ++pair;
+        while (rem >= upo) {
+            rem -= upo;
+            ++outer;
         }
     }
 };
 
-template <int FMT, int N, int XDT, bool FLOOR>
+template <int MODE>
+constexpr int max_x_rows() { return MODE == kCombine ? 8 : 4; }
+
+template <int FMT, int N, int XDT, bool FLOOR, int MODE>
 __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
     using G = Geo<N>;
-    __shared__ XLds<N> X[kMaxSpan];
+    constexpr int kMaxX = max_x_rows<MODE>();
+    __shared__ XLds<N> X[kMaxX];
     __shared__ uint2 grid_s[FMT == IQK_IQ1_S_R4 ? 2048 : 1];
 
     const int nthreads = blockDim.x;
@@ -532,24 +561,31 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nwaves = nthreads >> 6;
     const int bid = blockIdx.x;
-    // The call's rows, pair after pair, are cut into reduction groups that
-    // never straddle a pair; block b takes an equal share of the groups, so
-    // every CU gets the same number of rows whatever T * k is.
-    const int g0 = bid * p.gbase + min(bid, p.grem);
-    const int g1 = g0 + p.gbase + (bid < p.grem ? 1 : 0);
-    const int p_first = (int)fdiv((uint32_t)g0, p.dgpp);
-    const int p_last = (int)fdiv((uint32_t)(g1 - 1), p.dgpp);
+    // Units are cut evenly over the blocks (kCombine: over the bpt blocks of
+    // each token), so every CU gets the same number of rows.
+    int u0, u1;
+    if constexpr (MODE == kCombine) {
+        const int t = (int)fdiv((uint32_t)bid, p.dbpt);
+        const int lb = bid - t * p.bpt;
+        u0 = t * p.upo + lb * p.ubase + min(lb, p.urem);
+        u1 = u0 + p.ubase + (lb < p.urem ? 1 : 0);
+    } else {
+        u0 = bid * p.ubase + min(bid, p.urem);
+        u1 = u0 + p.ubase + (bid < p.urem ? 1 : 0);
+    }
+    constexpr bool kSlots = MODE == kCombine;   // k items per unit
+    const int kk = kSlots ? p.k : 1;
+    const int o_first = (int)fdiv((uint32_t)u0, p.dupo);
+    const int o_last = (int)fdiv((uint32_t)(u1 - 1), p.dupo);
+    auto pair_of = [&](int outer, int j) { return kSlots ? outer * p.k + j : outer; };
     // activation row of a pair: x[t] when shared by the k slots, else x[t, j]
     auto xrow_of = [&](int pair) { return p.x_slots == 1 ? (int)fdiv((uint32_t)pair, p.dk) : pair; };
-    const int xr0 = xrow_of(p_first);
-    const int nx = xrow_of(p_last) - xr0 + 1;
-    int ev[kMaxSpan];
-#pragma unroll
-    for (int i = 0; i < kMaxSpan; ++i) ev[i] = p.ids[min(p_first + i, p_last)];
-    auto expert_of = [&](int pair) {
-        const int d = pair - p_first;
-        return d == 0 ? ev[0] : (d == 1 ? ev[1] : (d == 2 ? ev[2] : ev[3]));
-    };
+    const int xr0 = xrow_of(pair_of(o_first, 0));
+    const int nx = xrow_of(pair_of(o_last, kk - 1)) - xr0 + 1;
+    // warm the scalar cache with the block's first ids (and weights)
+    const int id_first = p.ids[pair_of(o_first, 0)];
+    float rw_first = 0.f;
+    if constexpr (MODE == kCombine) rw_first = p.rw[pair_of(o_first, 0)];
 
     const int c = lane % G::LPR;  // chunk of k owned by this lane
     const int lane_row = lane / G::LPR;
@@ -580,26 +616,38 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
     }
     lds_barrier();
 
-    const int ngroups = g1 - g0;
-    const int my_groups = wave < ngroups ? (ngroups - wave + nwaves - 1) / nwaves : 0;
-    if (my_groups == 0) return;
-    Cursor lc;  // next group to load
-    lc.pair = (int)fdiv((uint32_t)(g0 + wave), p.dgpp);
-    lc.rem = g0 + wave - lc.pair * p.gpp;
-    Cursor pc = lc;  // next group to process
+    const int nunits = u1 - u0;
+    const int my_units = wave < nunits ? (nunits - wave + nwaves - 1) / nwaves : 0;
+    if (my_units == 0) return;
+    const int my_items = my_units * kk;
+    Cursor lc;  // next item to load
+    lc.outer = (int)fdiv((uint32_t)(u0 + wave), p.dupo);
+    lc.rem = u0 + wave - lc.outer * p.upo;
+    lc.j = 0;
+    Cursor pc = lc;  // next item to process
 
-    // Loads of a group past the wave's last use a zero-record resource.
-    auto load_next = [&](Group<FMT, N>& buf, bool live) {
-        const ExpertRes res = expert_res<FMT, N>(p, live ? expert_of(lc.pair) : -1);
-        load_group<FMT, N>(buf, res, lc.rem * G::RPG, lane_row, c);
-        lc.advance(nwaves, p.gpp);
+    constexpr int kHalf = G::RPG / 2;
+    const int half_out = p.out >> 1;
+    // expert row of local row q of the unit `rem`
+    auto unit_row = [&](int rem, int q) {
+        if constexpr (MODE == kSwiGLU) return q < kHalf ? rem * kHalf + q : half_out + rem * kHalf + (q - kHalf);
+        else return rem * G::RPG + q;
     };
-    // The first two groups of rows are requested only now: issued earlier, the
+    auto expert_of = [&](int pair) { return pair == pair_of(o_first, 0) ? id_first : p.ids[pair]; };
+
+    // Loads of an item past the wave's last use a zero-record resource.
+    auto load_next = [&](Group<FMT, N>& buf, bool live) {
+        const ExpertRes res = expert_res<FMT, N>(p, live ? expert_of(pair_of(lc.outer, lc.j)) : -1);
+        const int rem = lc.rem;
+        load_group<FMT, N>(buf, res, [&](int q) { return unit_row(rem, q); }, lane_row, c);
+        lc.advance(nwaves, p.upo, kk);
+    };
+    // The first two items' rows are requested only now: issued earlier, the
     // launch's row traffic would queue ahead of the activation reads and
     // hold every wave at the barrier until most rows had streamed in.
     Group<FMT, N> bufA, bufB;
     load_next(bufA, true);
-    load_next(bufB, my_groups > 1);
+    load_next(bufB, my_items > 1);
 
     uint32_t xh[16], xl[16];
     float lane_scale = 0.f;
@@ -621,10 +669,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
         cur_x = xi;
     };
 
+    float acc = 0.f;  // kCombine: running sum over the unit's slots
     auto process = [&](const Group<FMT, N>& gb) {
-        const int pair = pc.pair;
-        const int grp_row0 = pc.rem * G::RPG;
-        pc.advance(nwaves, p.gpp);
+        const int outer = pc.outer;
+        const int rem = pc.rem;
+        const int j = pc.j;
+        pc.advance(nwaves, p.upo, kk);
+        const int pair = pair_of(outer, j);
         const bool valid = (unsigned)expert_of(pair) < (unsigned)p.E;
         const int xi = xrow_of(pair) - xr0;
         if (xi != cur_x) load_x(xi);
@@ -639,87 +690,125 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
                 part[it] = __float_as_uint(f * (half_to_float(gb.r[it].d) * lane_scale));
             }
         }
-        int row_in_grp;
+        int q;
         bool writer;
-        uint32_t sum = reduce_group<N, FLOOR>(part, lane, &row_in_grp, &writer);
+        uint32_t sum = reduce_group<N, FLOOR>(part, lane, &q, &writer);
         // invalid id: its rows read zeros; they are reported as NaN (all ones
         // in the floor variant)
         if (!valid) sum = FLOOR ? 0xFFFFFFFFu : 0x7FC00000u;
-        const int r = grp_row0 + row_in_grp;
-        void* ybase = FLOOR ? (void*)(p.sink + (int64_t)pair * p.out) : (void*)(p.y + (int64_t)pair * p.out);
-        const Rsrc yres = make_rsrc(ybase, (uint32_t)p.out * 4u);
-        __builtin_amdgcn_raw_buffer_store_b32(sum, yres, writer ? (uint32_t)r * 4u : kOob, 0, 0);
+        if constexpr (MODE == kPlain) {
+            const int r = unit_row(rem, q);
+            void* ybase = FLOOR ? (void*)(p.sink + (int64_t)pair * p.out) : (void*)(p.y + (int64_t)pair * p.out);
+            const Rsrc yres = make_rsrc(ybase, (uint32_t)p.out * 4u);
+            __builtin_amdgcn_raw_buffer_store_b32(sum, yres, writer ? (uint32_t)r * 4u : kOob, 0, 0);
+        } else if constexpr (MODE == kSwiGLU) {
+            // gate row q < RPG/2 and its up row q + RPG/2 sit 32 lanes apart
+            // (16 when a row spans 32 lanes)
+            const uint32_t up = (uint32_t)__shfl_xor((int)sum, G::LPR == 32 ? 16 : 32);
+            const float g = __uint_as_float(sum);
+            const float hv = g / (1.0f + expf(-g)) * __uint_as_float(up);
+            const int r = rem * kHalf + q;  // h index inside the pair
+            const Rsrc hres = make_rsrc(p.h + (int64_t)pair * half_out, (uint32_t)half_out * 2u);
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16(hv), hres,
+                                                  writer && q < kHalf ? (uint32_t)r * 2u : kOob, 0, 0);
+        } else {
+            const float w = j == 0 && outer == o_first ? rw_first : p.rw[pair];
+            const float contrib = w * __uint_as_float(sum);
+            acc = j == 0 ? contrib : acc + contrib;
+            const int r = unit_row(rem, q);
+            const Rsrc yres = make_rsrc(p.y + (int64_t)outer * p.out, (uint32_t)p.out * 4u);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), yres,
+                                                  writer && j == kk - 1 ? (uint32_t)r * 4u : kOob, 0, 0);
+        }
     };
 
-    // Groups 0 and 1 are in flight.  The loop refills a buffer just before
-    // processing the other one, so at its top exactly one group's loads are
-    // outstanding on every path and each wait covers only the group it needs.
-    load_x(xrow_of(pc.pair) - xr0);
+    // Items 0 and 1 are in flight.  The loop refills a buffer just before
+    // processing the other one, so at its top exactly one item's loads are
+    // outstanding on every path and each wait covers only the item it needs.
+    load_x(xrow_of(pair_of(pc.outer, pc.j)) - xr0);
     process(bufA);
     if constexpr (FMT == IQK_IQ1_S_R4) {
-        // measured: at one or two groups per wave the IQ1_S_R4 instance is
+        // measured: at one or two items per wave the IQ1_S_R4 instance is
         // faster without the loop's dead refills (the 2-bit ones are not)
-        if (my_groups <= 2) {
-            if (my_groups == 2) process(bufB);
+        if (my_items <= 2) {
+            if (my_items == 2) process(bufB);
             return;
         }
     }
-    for (int i = 1; i < my_groups; i += 2) {
-        load_next(bufA, i + 1 < my_groups);
+    for (int i = 1; i < my_items; i += 2) {
+        load_next(bufA, i + 1 < my_items);
         process(bufB);
-        load_next(bufB, i + 2 < my_groups);
-        if (i + 1 >= my_groups) break;
+        load_next(bufB, i + 2 < my_items);
+        if (i + 1 >= my_items) break;
         process(bufA);
     }
 }
 
-template <int FMT, int N, int XDT, bool FLOOR>
-hipError_t launch_inst(GemvParams p, int64_t pairs, hipStream_t s) {
+template <int FMT, int N, int XDT, bool FLOOR, int MODE>
+hipError_t launch_inst(GemvParams p, int64_t T, hipStream_t s) {
     using G = Geo<N>;
-    // one large workgroup per CU over the whole call; more blocks only when
-    // a block would otherwise span more than kMaxSpan pairs (small out)
-    const int64_t gpp = (p.out + G::RPG - 1) / G::RPG;
-    const int64_t total = pairs * gpp;
+    // units: rows of one outer in reduction groups (kSwiGLU: RPG/2 output rows)
+    const int64_t out_rows = MODE == kSwiGLU ? p.out / 2 : p.out;
+    const int64_t rows_per_unit = MODE == kSwiGLU ? G::RPG / 2 : G::RPG;
+    const int64_t upo = (out_rows + rows_per_unit - 1) / rows_per_unit;
+    const int64_t outers = MODE == kCombine ? T : T * p.k;
+    const int64_t total = outers * upo;
     if (total <= 0 || total > 0x7FFFFFFF) return hipErrorInvalidValue;
-    int64_t nb = total < IQK_GEMV_TARGET_BLOCKS ? total : IQK_GEMV_TARGET_BLOCKS;
-    // a block of at most (kMaxSpan - 1) * gpp + 1 groups touches at most kMaxSpan pairs
-    const int64_t span_groups = (kMaxSpan - 1) * gpp + 1;
-    const int64_t nb_span = (total + span_groups - 1) / span_groups;
-    nb = nb < nb_span ? nb_span : nb;
-    const int64_t groups = (total + nb - 1) / nb;  // reduction groups of the largest block
+    int64_t nb, bpt = 1;
+    if constexpr (MODE == kCombine) {
+        // blocks never straddle tokens: a block holds one token's k activation rows
+        bpt = IQK_GEMV_TARGET_BLOCKS / T;
+        bpt = bpt < 1 ? 1 : (bpt > upo ? upo : bpt);
+        nb = T * bpt;
+        p.ubase = (int32_t)(upo / bpt);
+        p.urem = (int32_t)(upo % bpt);
+    } else {
+        // one large workgroup per CU over the whole call; more blocks only
+        // when a block would otherwise span more than max_x_rows pairs
+        nb = total < IQK_GEMV_TARGET_BLOCKS ? total : IQK_GEMV_TARGET_BLOCKS;
+        // a block of at most (span - 1) * upo + 1 units touches at most span outers
+        const int64_t span_units = (max_x_rows<MODE>() - 1) * upo + 1;
+        const int64_t nb_span = (total + span_units - 1) / span_units;
+        nb = nb < nb_span ? nb_span : nb;
+        p.ubase = (int32_t)(total / nb);
+        p.urem = (int32_t)(total % nb);
+    }
+    const int64_t units = MODE == kCombine ? (upo + bpt - 1) / bpt : (total + nb - 1) / nb;  // largest block
+    const int64_t items = MODE == kCombine ? units * p.k : units;
     // waves: a multiple of four (one share per SIMD) up to 16, at least
-    // IQK_GEMV_MIN_GROUPS groups each once the block is large enough
-    int64_t waves = (groups + IQK_GEMV_MIN_GROUPS - 1) / IQK_GEMV_MIN_GROUPS;
-    waves = groups < 4 ? groups : ((waves + 3) / 4) * 4;
+    // IQK_GEMV_MIN_GROUPS items each once the block is large enough
+    int64_t waves = (items + IQK_GEMV_MIN_GROUPS - 1) / IQK_GEMV_MIN_GROUPS;
+    waves = items < 4 ? items : ((waves + 3) / 4) * 4;
     waves = waves > kMaxWaves ? kMaxWaves : (waves < 1 ? 1 : waves);
-    p.pairs = (int32_t)pairs;
-    p.gpp = (int32_t)gpp;
-    p.gbase = (int32_t)(total / nb);
-    p.grem = (int32_t)(total % nb);
-    p.dgpp = make_fastdiv((uint32_t)gpp);
+    if (MODE == kCombine && waves > units) waves = units;  // a unit's slots stay in one wave
+    p.outers = (int32_t)outers;
+    p.upo = (int32_t)upo;
+    p.bpt = (int32_t)bpt;
+    p.dupo = make_fastdiv((uint32_t)upo);
     p.dk = make_fastdiv((uint32_t)p.k);
-    hipLaunchKernelGGL((gemv_kernel<FMT, N, XDT, FLOOR>), dim3((unsigned)nb), dim3((unsigned)(64 * waves)), 0, s, p);
+    p.dbpt = make_fastdiv((uint32_t)bpt);
+    hipLaunchKernelGGL((gemv_kernel<FMT, N, XDT, FLOOR, MODE>), dim3((unsigned)nb), dim3((unsigned)(64 * waves)), 0, s, p);
     return hipGetLastError();
 }
 
-template <int FMT, int N, bool FLOOR>
-hipError_t launch_x(const GemvParams& p, int xdt, int64_t pairs, hipStream_t s) {
-    if (xdt == IQK_BF16) return launch_inst<FMT, N, IQK_BF16, FLOOR>(p, pairs, s);
-    return launch_inst<FMT, N, IQK_F32, FLOOR>(p, pairs, s);
+template <int FMT, int N, bool FLOOR, int MODE>
+hipError_t launch_x(const GemvParams& p, int xdt, int64_t T, hipStream_t s) {
+    if (xdt == IQK_BF16) return launch_inst<FMT, N, IQK_BF16, FLOOR, MODE>(p, T, s);
+    return launch_inst<FMT, N, IQK_F32, FLOOR, MODE>(p, T, s);
 }
 
-template <int FMT, bool FLOOR>
-hipError_t launch_n(const GemvParams& p, int64_t n, int xdt, int64_t pairs, hipStream_t s) {
-    if (n == 4096) return launch_x<FMT, 4096, FLOOR>(p, xdt, pairs, s);
-    if (n == 2048) return launch_x<FMT, 2048, FLOOR>(p, xdt, pairs, s);
-    return launch_x<FMT, 512, FLOOR>(p, xdt, pairs, s);
+template <int FMT, bool FLOOR, int MODE>
+hipError_t launch_n(const GemvParams& p, int64_t n, int xdt, int64_t T, hipStream_t s) {
+    if (n == 4096) return launch_x<FMT, 4096, FLOOR, MODE>(p, xdt, T, s);
+    if (n == 2048) return launch_x<FMT, 2048, FLOOR, MODE>(p, xdt, T, s);
+    return launch_x<FMT, 512, FLOOR, MODE>(p, xdt, T, s);
 }
 
-template <bool FLOOR>
-hipError_t launch_fmt(const GemvParams& p, int fmt, int64_t n, int xdt, int64_t pairs, hipStream_t s) {
-    if (fmt == IQK_IQ2_KS) return launch_n<IQK_IQ2_KS, FLOOR>(p, n, xdt, pairs, s);
-    if (fmt == IQK_IQ2_K) return launch_n<IQK_IQ2_K, FLOOR>(p, n, xdt, pairs, s);
-    return launch_n<IQK_IQ1_S_R4, FLOOR>(p, n, xdt, pairs, s);
+template <bool FLOOR, int MODE>
+hipError_t launch_fmt(const GemvParams& p, int fmt, int64_t n, int xdt, int64_t T, hipStream_t s) {
+    if (fmt == IQK_IQ2_KS) return launch_n<IQK_IQ2_KS, FLOOR, MODE>(p, n, xdt, T, s);
+    if (fmt == IQK_IQ2_K) return launch_n<IQK_IQ2_K, FLOOR, MODE>(p, n, xdt, T, s);
+    return launch_n<IQK_IQ1_S_R4, FLOOR, MODE>(p, n, xdt, T, s);
 }
 
 }  // namespace
@@ -744,10 +833,13 @@ hipError_t launch_gemv(const GemvLaunch& a, bool floor_variant, hipStream_t s) {
     p.ids = a.ids;
     p.y = a.y;
     p.sink = a.sink;
-    p.pairs = p.gpp = p.gbase = p.grem = 0;
-    const int64_t pairs = a.T * a.k;
-    return floor_variant ? launch_fmt<true>(p, a.fmt, a.n, a.x_dtype, pairs, s)
-                         : launch_fmt<false>(p, a.fmt, a.n, a.x_dtype, pairs, s);
+    p.h = a.h;
+    p.rw = a.route_w;
+    p.outers = p.upo = p.ubase = p.urem = p.bpt = 0;
+    if (floor_variant) return launch_fmt<true, kPlain>(p, a.fmt, a.n, a.x_dtype, a.T, s);
+    if (a.mode == kSwiGLU) return launch_fmt<false, kSwiGLU>(p, a.fmt, a.n, a.x_dtype, a.T, s);
+    if (a.mode == kCombine) return launch_fmt<false, kCombine>(p, a.fmt, a.n, a.x_dtype, a.T, s);
+    return launch_fmt<false, kPlain>(p, a.fmt, a.n, a.x_dtype, a.T, s);
 }
 
 }  // namespace iqk

@@ -272,6 +272,10 @@ int check_gemv_args(const iqk_weights* w, const float* values, const int8_t* gri
     if (T * k > 65535LL * 64) return fail(IQK_E_ARG, "T*k = %lld exceeds the decode limit", (long long)(T * k));
     if (x_slots != 1 && x_slots != k) return fail(IQK_E_ARG, "x_slots must be 1 or k");
     // the kernel indexes 4-row reduction groups of the whole call in 32 bits
+    // one expert's plane, and one output row set, is addressed with 32-bit
+    // byte offsets
+    if (w->out * (int64_t)iqk::row_bytes(w->fmt, w->in) > 0x7FFFFFFFLL)
+        return fail(IQK_E_ARG, "decode matvec needs out * row bytes < 2^31 (out = %lld)", (long long)w->out);
     if (T * k * ((w->out + 3) / 4) > 0x7FFFFFFFLL)
         return fail(IQK_E_ARG, "T*k*ceil(out/4) = %lld exceeds 2^31 - 1", (long long)(T * k * ((w->out + 3) / 4)));
     if (x_dtype != IQK_F32 && x_dtype != IQK_BF16) return fail(IQK_E_ARG, "x_dtype must be IQK_F32 or IQK_BF16");
@@ -300,6 +304,9 @@ int check_gemv_args(const iqk_weights* w, const float* values, const int8_t* gri
     L->k = k;
     L->y = nullptr;
     L->sink = nullptr;
+    L->mode = 0;
+    L->h = nullptr;
+    L->route_w = nullptr;
     return IQK_OK;
 }
 
@@ -394,6 +401,37 @@ int iqk_moe_gemv(const iqk_weights* w, const float* values, const int8_t* grid, 
     if (T == 0) return ok();
     hipError_t e = iqk::launch_gemv(L, false, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode matvec launch");
+    return ok();
+}
+
+int iqk_moe_gemv_swiglu(const iqk_weights* w, const float* values, const int8_t* grid, const void* x, int x_dtype,
+                        int x_slots, const int32_t* ids, int64_t T, int k, uint16_t* h, void* stream) {
+    iqk::GemvLaunch L;
+    int rc = check_gemv_args(w, values, grid, x, x_dtype, x_slots, ids, T, k, h, &L);
+    if (rc) return rc;
+    if (w->out % 2) return fail(IQK_E_SHAPE, "SwiGLU needs an even number of gate/up rows (out = %lld)", (long long)w->out);
+    L.mode = 1;
+    L.h = h;
+    if (T == 0) return ok();
+    hipError_t e = iqk::launch_gemv(L, false, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "SwiGLU matvec launch");
+    return ok();
+}
+
+int iqk_moe_gemv_combine(const iqk_weights* w, const float* values, const int8_t* grid, const void* x, int x_dtype,
+                         int x_slots, const int32_t* ids, const float* route_w, int64_t T, int k, float* y,
+                         void* stream) {
+    iqk::GemvLaunch L;
+    int rc = check_gemv_args(w, values, grid, x, x_dtype, x_slots, ids, T, k, y, &L);
+    if (rc) return rc;
+    if (k > 8) return fail(IQK_E_ARG, "combine handles at most 8 slots per token (k = %d)", k);
+    if (T > 0 && !route_w) return fail(IQK_E_ARG, "null router weights");
+    L.mode = 2;
+    L.y = y;
+    L.route_w = route_w;
+    if (T == 0) return ok();
+    hipError_t e = iqk::launch_gemv(L, false, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "combine matvec launch");
     return ok();
 }
 

@@ -79,7 +79,10 @@ struct GemvLaunch {
     int64_t T;
     int k;
     float* y;
-    uint32_t* sink;  // floor variant output (y unused)
+    uint32_t* sink;          // floor variant output (y unused)
+    int mode;                // 0 plain y[T,k,out], 1 SwiGLU h[T,k,out/2] bf16, 2 combine y[T,out]
+    uint16_t* h;             // mode 1
+    const float* route_w;    // mode 2: [T, k]
 };
 
 struct RouteLaunch {

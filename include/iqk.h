@@ -142,10 +142,33 @@ int iqk_dequant(const iqk_weights* w, int64_t row0, int64_t nrows, const float* 
  * 64-value block as 15-bit fixed point (relative error about 2^-14 of the
  * block maximum); weights and sums are exact integers up to one float32
  * rounding per row; ||y - y_exact|| / ||y_exact|| <= 1e-3.
- * Limits: T * k <= 65535 * 64. */
+ * Limits: T * k <= 65535 * 64, out * iqk_row_bytes(fmt, in) < 2^31,
+ * T * k * ceil(out / 4) < 2^31 (IQK_E_ARG otherwise). */
 int iqk_moe_gemv(const iqk_weights* w, const float* values, const int8_t* grid,
                  const void* x, int x_dtype, int x_slots, const int32_t* ids,
                  int64_t T, int k, float* y, void* stream);
+
+/* The MoE layer step after gate/up (the projection-level interface of
+ * "Surface" used the way a SwiGLU expert uses it): the same matvec over a
+ * gate/up tensor whose rows [0, I) are gate and [I, 2I) up (out = 2I, even,
+ * else IQK_E_SHAPE), written as h[t, j, i] = silu(g) * u with
+ * g = gate_i . x, u = up_i . x, silu(g) = g / (1 + exp(-g)) in float32, and
+ * h stored as bf16 (round to nearest even): device uint16 [T, k, I].  This is
+ * the down projection's per-pair input.  Invalid ids give NaN rows.
+ * Arguments and limits otherwise as iqk_moe_gemv. */
+int iqk_moe_gemv_swiglu(const iqk_weights* w, const float* values, const int8_t* grid,
+                        const void* x, int x_dtype, int x_slots, const int32_t* ids,
+                        int64_t T, int k, uint16_t* h, void* stream);
+
+/* The MoE layer step after down: router-weighted combine of the k routed
+ * experts, y[t, o] = sum_{j=0..k-1} route_w[t, j] * (W_{ids[t,j]}[o, :] .
+ * x[t, s, :]), summed in float32 in slot order (s as in iqk_moe_gemv).
+ * route_w: device float32 [T, k]; y: device float32 [T, out].  An invalid
+ * id makes its token's row NaN.  k <= 8 (IQK_E_ARG); otherwise as
+ * iqk_moe_gemv.  Deterministic: one wave owns each (token, row group). */
+int iqk_moe_gemv_combine(const iqk_weights* w, const float* values, const int8_t* grid,
+                         const void* x, int x_dtype, int x_slots, const int32_t* ids,
+                         const float* route_w, int64_t T, int k, float* y, void* stream);
 
 /* Routing gather ("Surface": sorting pairs by expert so that each expert's
  * weights are read once).  ids: device int32 [P] (P = T*k pair indices

@@ -9,6 +9,11 @@ reconstruction chain in the order the "mlx-iqk" package description's
 "Format" section gives, double accumulation for products).  This module is
 argument marshalling only.
 
+MoE-layer glue on either side of the projections (``swiglu``, ``combine``)
+is not on the pages: it is the standard SwiGLU expert MLP and the
+router-weighted sum of the routed experts, written here as their plain
+float64 definitions in numpy.
+
 Parity pins: every function here is checked in ``tests/test_oracle_*.py``
 against hand-computed blocks, exact closed forms, library routines (numpy /
 torch casts, numpy float64 matmul, numpy stable argsort) and bijection
@@ -246,3 +251,30 @@ def route(ids: np.ndarray, E: int):
     perm = np.zeros(max(ids.size, 1), np.int32)
     bad = lib().orc_route(_ptr(ids), ids.size, E, _ptr(counts), _ptr(offsets), _ptr(perm))
     return counts, offsets, perm[: ids.size - bad], int(bad)
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    """g * sigmoid(g) = g / (1 + exp(-g)) in float64 (exp overflow gives -0.0)."""
+    g = np.asarray(g, np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu(gate_up: np.ndarray) -> np.ndarray:
+    """SwiGLU expert activation: the last axis holds the gate rows [0, I)
+    then the up rows [I, 2I); returns silu(gate) * up, shape [..., I]."""
+    gu = np.asarray(gate_up, np.float64)
+    I = gu.shape[-1] // 2
+    return silu(gu[..., :I]) * gu[..., I:2 * I]
+
+
+def combine(y_pairs: np.ndarray, route_w: np.ndarray) -> np.ndarray:
+    """Router-weighted combine: y[t] = sum_j route_w[t, j] * y_pairs[t, j, :]
+    (float64; a NaN in any slot makes the token's row NaN)."""
+    yp = np.asarray(y_pairs, np.float64)
+    w = np.asarray(route_w, np.float64)
+    T, k = w.shape
+    out = np.zeros((T, yp.shape[-1]), np.float64)
+    for j in range(k):
+        out += w[:, j:j + 1] * yp[:, j, :]
+    return out

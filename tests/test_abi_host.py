@@ -112,6 +112,14 @@ def test_validation_errors_before_any_launch():
     assert L.iqk_moe_gemv(ctypes.byref(w), halves.ctypes.data_as(P), None, fake, 2, 1, fake, 0, 6, fake, s0) == 0
     big = np.array([128, 0, 0, 0, 0, 0, 0, 1], np.float32)   # 128 * 2^0 and 1: no common exponent fits int8
     assert L.iqk_moe_gemv(ctypes.byref(w), big.ctypes.data_as(P), None, fake, 2, 1, fake, 0, 6, fake, s0) == q._E_TABLE
+    # layer glue: SwiGLU needs an even gate/up row count; combine at most 8 slots
+    w = _wdesc(K, 2, 9, 2048)
+    assert L.iqk_moe_gemv_swiglu(ctypes.byref(w), vp, None, fake, 2, 1, fake, 0, 6, fake, s0) == q._E_SHAPE
+    w = _wdesc(K, 2, 8, 2048)
+    assert L.iqk_moe_gemv_swiglu(ctypes.byref(w), vp, None, fake, 2, 1, fake, 0, 6, fake, s0) == 0
+    assert L.iqk_moe_gemv_combine(ctypes.byref(w), vp, None, fake, 2, 9, fake, fake, 0, 9, fake, s0) == q._E_ARG
+    assert L.iqk_moe_gemv_combine(ctypes.byref(w), vp, None, fake, 2, 6, fake, None, 1, 6, fake, s0) == q._E_ARG
+    assert L.iqk_moe_gemv_combine(ctypes.byref(w), vp, None, fake, 2, 6, fake, fake, 0, 6, fake, s0) == 0
     # dequant
     w = _wdesc(K, 2, 8, 512)
     assert L.iqk_dequant(ctypes.byref(w), 10, 10, vp, None, 2, fake, s0) == q._E_ARG  # rows out of range

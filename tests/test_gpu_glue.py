@@ -1,0 +1,110 @@
+"""GPU parity of the MoE-layer glue entry points against the oracle.
+
+iqk_moe_gemv_swiglu: h = silu(gate . x) * (up . x) stored as bf16; bar:
+per-vector relative error <= 5e-3 (bf16 storage is a half-ulp of 2^-9
+relative on top of the matvec's 1e-3).  iqk_moe_gemv_combine:
+y[t] = sum_j w[t, j] W_j x_j in float32; bar: |y - ref| <= 1e-3 *
+sum_j |w_j| ||W_j x_j|| per token (the combine may cancel, so the bound is
+taken on the parts)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import dequant_iqk_moe_amd as q
+from gpu_common import TOL_GEMV, announce, bf16_round, rel_err_per_vector, to_dev
+
+pytestmark = pytest.mark.gpu
+
+KS, K, R4 = 1, 2, 3
+TOL_SWIGLU = 5e-3
+
+
+def _weights(fmt, E, out, n, seed):
+    wire = synth.wire(fmt, E * out, n, seed)
+    return q.Weights.from_wire(fmt, E, out, n, wire), oracle.pack(fmt, wire, E * out, n)
+
+
+def _inputs(seed, T, k, E, x_slots, n):
+    ids = synth.topk_ids(T, k, E, seed + 3)
+    x = bf16_round(synth.normal((T, x_slots, n), seed + 4))
+    return ids, x
+
+
+@pytest.mark.parametrize("fmt", [KS, K, R4])
+@pytest.mark.parametrize("n,I,T,k,E,x_slots", [
+    (4096, 64, 3, 6, 16, 1),
+    (2048, 36, 2, 4, 8, 4),     # ragged: 36 rows in units of 2 gate + 2 up rows
+    (512, 20, 5, 3, 6, 1),      # 8-row units: 4 gate + 4 up rows per wave iteration
+    (4096, 2048, 1, 6, 12, 1),  # the gate/up geometry, fewer experts
+])
+def test_swiglu_parity(fmt, n, I, T, k, E, x_slots):
+    seed = 700 + fmt + n // 256 + I
+    announce(f"swiglu fmt={fmt} n={n} I={I} T={T} k={k} E={E} slots={x_slots}")
+    w, s = _weights(fmt, E, 2 * I, n, seed)
+    values, grid = synth.values_table(seed + 1), synth.ternary_grid(seed + 2)
+    ids, x = _inputs(seed, T, k, E, x_slots, n)
+    h = q.moe_gemv_swiglu(w, to_dev(x, torch.bfloat16), to_dev(ids), values, to_dev(grid), x_slots=x_slots)
+    h = h.float().cpu().numpy()
+    ref = oracle.swiglu(oracle.moe(fmt, s, E, 2 * I, n, x, ids, values, grid, x_slots=x_slots))
+    assert h.shape == (T, k, I)
+    err = rel_err_per_vector(h, ref)
+    assert np.all(err <= TOL_SWIGLU), err.max()
+
+
+@pytest.mark.parametrize("fmt", [KS, K, R4])
+@pytest.mark.parametrize("n,out,T,k,E,x_slots", [
+    (2048, 72, 3, 6, 8, 6),
+    (4096, 40, 5, 4, 10, 1),    # shared input: sum_j w_j W_j x
+    (512, 24, 7, 8, 12, 8),     # k = 8, the most slots
+    (2048, 4100, 1, 6, 8, 6),   # ragged tail, one token over many blocks
+    (2048, 16, 40, 6, 9, 6),    # many tokens, few rows: one block per token
+])
+def test_combine_parity(fmt, n, out, T, k, E, x_slots):
+    seed = 800 + fmt + n // 256 + out
+    announce(f"combine fmt={fmt} n={n} out={out} T={T} k={k} E={E} slots={x_slots}")
+    w, s = _weights(fmt, E, out, n, seed)
+    values, grid = synth.values_table(seed + 1), synth.ternary_grid(seed + 2)
+    ids, x = _inputs(seed, T, k, E, x_slots, n)
+    rw = np.random.default_rng(seed + 5).dirichlet(np.ones(k), size=T).astype(np.float32)
+    y = q.moe_gemv_combine(w, to_dev(x, torch.bfloat16), to_dev(ids), to_dev(rw), values, to_dev(grid),
+                           x_slots=x_slots).cpu().numpy()
+    parts = oracle.moe(fmt, s, E, out, n, x, ids, values, grid, x_slots=x_slots)
+    ref = oracle.combine(parts, rw)
+    scale = np.sum(np.abs(rw)[:, :, None] * np.linalg.norm(parts, axis=-1, keepdims=True), axis=1)[:, 0]
+    err = np.linalg.norm(y - ref, axis=-1) / scale
+    assert np.all(err <= TOL_GEMV), err.max()
+
+
+def test_combine_deterministic_and_invalid_ids():
+    fmt, n, out, E, T, k = K, 2048, 64, 10, 6, 6
+    w, s = _weights(fmt, E, out, n, 900)
+    values = synth.values_table(901)
+    ids, x = _inputs(900, T, k, E, k, n)
+    rw = np.random.default_rng(905).dirichlet(np.ones(k), size=T).astype(np.float32)
+    xd, rwd = to_dev(x, torch.bfloat16), to_dev(rw)
+    announce("combine determinism / invalid ids")
+    a = q.moe_gemv_combine(w, xd, to_dev(ids), rwd, values).cpu().numpy()
+    b = q.moe_gemv_combine(w, xd, to_dev(ids), rwd, values).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    bad = ids.copy()
+    bad[2, 4] = -1
+    bad[4, 0] = E
+    c = q.moe_gemv_combine(w, xd, to_dev(bad), rwd, values).cpu().numpy()
+    assert np.all(np.isnan(c[[2, 4]]))
+    keep = [0, 1, 3, 5]
+    assert np.array_equal(c[keep].view(np.uint32), a[keep].view(np.uint32))
+
+
+def test_swiglu_invalid_ids_give_nan_rows():
+    fmt, n, I, E = KS, 2048, 48, 5
+    w, s = _weights(fmt, E, 2 * I, n, 910)
+    values = synth.values_table(911)
+    ids = np.array([[0, 7, -1, 2]], np.int32)
+    x = bf16_round(synth.normal((1, 1, n), 912))
+    announce("swiglu invalid ids")
+    h = q.moe_gemv_swiglu(w, to_dev(x, torch.bfloat16), to_dev(ids), values).float().cpu().numpy()
+    assert np.all(np.isnan(h[0, 1])) and np.all(np.isnan(h[0, 2]))
+    ref = oracle.swiglu(oracle.moe(fmt, s, E, 2 * I, n, x, ids, values))
+    assert np.all(rel_err_per_vector(h[0, [0, 3]], ref[0, [0, 3]]) <= TOL_SWIGLU)
