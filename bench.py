@@ -168,6 +168,46 @@ def validate_sample(oracle, pool, ids, xin, y, slots, values, grid_host, rng, ro
     return worst
 
 
+def layer_cell(ctx, gate_up, down, x, S, reps, warm, seed):
+    """One MoE layer's routed experts at T=1 with the glue fused: gate/up
+    matvec + SwiGLU (bf16 h), then down matvec + router-weighted combine
+    (y [1, hidden]).  Validated in full against the oracle first."""
+    import synth
+    import oracle
+    q, torch = ctx.q, ctx.torch
+    T = 1
+    ids_host = [synth.topk_ids(T, K, E, seed * 1000 + i) for i in range(S)]
+    ids = [torch.from_numpy(a).cuda() for a in ids_host]
+    rw_host = np.random.default_rng(seed).dirichlet(np.ones(K), size=T).astype(np.float32)
+    rw = torch.from_numpy(rw_host).cuda()
+    hbuf = torch.empty((T, K, I), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    q.moe_gemv_swiglu(gate_up.w[0], x, ids[0], ctx.values, h=hbuf)
+    q.moe_gemv_combine(down.w[0], hbuf, ids[0], rw, ctx.values, y=y)
+    torch.cuda.synchronize()
+    xv = x.float().cpu().numpy().reshape(T, 1, H)
+    gu = oracle.moe(q.IQ2_K, gate_up.host_streams, E, 2 * I, H, xv, ids_host[0], ctx.values)
+    h_ref = oracle.swiglu(gu)
+    h_gpu = hbuf.float().cpu().numpy()
+    err_h = float(np.max(np.linalg.norm(h_gpu - h_ref, axis=-1) / np.linalg.norm(h_ref, axis=-1)))
+    parts = oracle.moe(q.IQ2_K, down.host_streams, E, H, I, h_gpu, ids_host[0], ctx.values, x_slots=K)
+    y_ref = oracle.combine(parts, rw_host)
+    scale = np.sum(np.abs(rw_host)[:, :, None] * np.linalg.norm(parts, axis=-1, keepdims=True), axis=1)[:, 0]
+    err_y = float(np.max(np.linalg.norm(y.cpu().numpy() - y_ref, axis=-1) / scale))
+
+    def run(i):
+        p = i % POOLS
+        q.moe_gemv_swiglu(gate_up.w[p], x, ids[i], ctx.values, h=hbuf)
+        q.moe_gemv_combine(down.w[p], hbuf, ids[i], rw, ctx.values, y=y)
+
+    ms = timed_graph(torch, run, S, reps, warm)
+    nbytes = float(np.mean([gate_up.bytes_for(a) + down.bytes_for(a) for a in ids_host])) + \
+        x.numel() * 2 + 2 * hbuf.numel() * 2 + y.numel() * 4 + rw.numel() * 4
+    return {"cell": "IQ2_K MoE layer T=1: gate/up+SwiGLU, down+combine", "kind": "layer",
+            "us": round(ms * 1e3, 3), "bytes": int(nbytes), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 2),
+            "tokens_per_s": round(T / (ms * 1e-3), 1), "validation_h": err_h, "validation_y": err_y}
+
+
 def decode_cell(ctx, pool, T, proj, S, reps, warm, seed):
     """one matvec cell: kernel time, floor time, stream-read time for the same bytes"""
     import synth
@@ -397,6 +437,7 @@ def main():
     cells = []
     if args.cells == "all":
         Sc, rc, wc = 32, 8, 2
+        cells.append(layer_cell(ctx, gate_up, down, x, Sc, rc, wc, 61))
         cells.append(decode_cell(ctx, gate_up, 1, "gate_up", Sc, rc, wc, 21))
         cells.append(decode_cell(ctx, down, 1, "down", Sc, rc, wc, 22))
         for fmt, Ts, sd in ((q.IQ2_KS, (1, 8), 3), (q.IQ1_S_R4, (1,), 4)):
@@ -418,7 +459,7 @@ def main():
                       "bytes": b1, "GBps": round(b1 / (ms1 * 1e-3) / 1e9, 2)})
         ctx.sbuf = None
         torch.cuda.empty_cache()
-        for fmt in (q.IQ2_K, q.IQ2_KS):
+        for fmt in (q.IQ2_K, q.IQ2_KS, q.IQ1_S_R4):
             cells.extend(prefill_cells(ctx, fmt, 500 + fmt))
         for c in cells:
             log(json.dumps(c))

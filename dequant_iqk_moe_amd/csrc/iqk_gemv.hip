@@ -51,10 +51,6 @@ namespace {
 #define IQK_GEMV_MAX_WAVES 16        // waves per workgroup (launch bound)
 #endif
 constexpr int kMaxWaves = IQK_GEMV_MAX_WAVES;
-// pairs one workgroup may span (the launch plan keeps every block within it);
-// each spanned activation row has its own fixed-point copy in LDS
-constexpr int kMaxSpan = 4;
-static_assert(kMaxSpan == 4, "expert_of selects among four ids");
 
 // Unsigned division by a launch constant d >= 1 without a division sequence
 // (the scalar unit has no divide; the compiler's expansion is ~40
@@ -530,21 +526,36 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 
 // Position of one item: its outer index (pair, or token for kCombine), its
 // unit inside the outer, and the slot j (kCombine).  Items of a wave are
-// visited in increasing order, units nwaves apart, so the cursor advances
-// without a division.
+// visited in increasing order, nwaves apart, so the cursor advances without
+// a division: units step through the outers (kPlain, kSwiGLU), slots step
+// through the units of the block's one token (kCombine).
 struct Cursor {
     int outer, rem, j;
-    __device__ __forceinline__ void advance(int step, int upo, int kk) {
-        if (++j < kk) return;
-        j = 0;
-        rem += step;
-        while (rem >= upo) {
-            rem -= upo;
-            ++outer;
+    template <int MODE>
+    __device__ __forceinline__ void advance(int step, int upo, int k) {
+        if constexpr (MODE == kCombine) {
+            j += step;
+            while (j >= k) {
+                j -= k;
+                ++rem;
+            }
+        } else {
+            rem += step;
+            while (rem >= upo) {
+                rem -= upo;
+                ++outer;
+            }
         }
     }
 };
 
+// kCombine: units per block at most, so the per-slot partial sums of a block
+// fit in LDS (units * k * rows per unit floats)
+constexpr int kCombineMaxUnits = 64;
+
+// Pairs (and activation rows) one workgroup may span; the launch plan keeps
+// every block within it.  Each spanned activation row has its own
+// fixed-point copy in LDS.
 template <int MODE>
 constexpr int max_x_rows() { return MODE == kCombine ? 8 : 4; }
 
@@ -577,15 +588,21 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
     const int kk = kSlots ? p.k : 1;
     const int o_first = (int)fdiv((uint32_t)u0, p.dupo);
     const int o_last = (int)fdiv((uint32_t)(u1 - 1), p.dupo);
+    __shared__ float part_s[MODE == kCombine ? kCombineMaxUnits * 8 * 8 : 1];  // [unit][slot][row]
     auto pair_of = [&](int outer, int j) { return kSlots ? outer * p.k + j : outer; };
     // activation row of a pair: x[t] when shared by the k slots, else x[t, j]
     auto xrow_of = [&](int pair) { return p.x_slots == 1 ? (int)fdiv((uint32_t)pair, p.dk) : pair; };
     const int xr0 = xrow_of(pair_of(o_first, 0));
     const int nx = xrow_of(pair_of(o_last, kk - 1)) - xr0 + 1;
-    // warm the scalar cache with the block's first ids (and weights)
-    const int id_first = p.ids[pair_of(o_first, 0)];
-    float rw_first = 0.f;
-    if constexpr (MODE == kCombine) rw_first = p.rw[pair_of(o_first, 0)];
+    // The ids (and router weights) of every pair the block touches, staged
+    // in LDS at the start: read from memory later, after the first result
+    // store, every read would be a vector load that waits for all the row
+    // loads in flight.
+    constexpr int kPairs = max_x_rows<MODE>();
+    __shared__ int32_t ids_s[kPairs];
+    __shared__ float rw_s[kPairs];
+    const int pr0 = pair_of(o_first, 0);
+    const int pr_last = pair_of(o_last, kk - 1);
 
     const int c = lane % G::LPR;  // chunk of k owned by this lane
     const int lane_row = lane / G::LPR;
@@ -606,7 +623,17 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
         if (tid < 1024) gw0 = gsrc[tid];
         if (tid + nthreads < 1024) gw1 = gsrc[tid + nthreads];
     }
+    int32_t id_v = 0;
+    float rw_v = 0.f;
+    if (tid < kPairs) {
+        id_v = p.ids[min(pr0 + tid, pr_last)];
+        if constexpr (MODE == kCombine) rw_v = p.rw[min(pr0 + tid, pr_last)];
+    }
     if (tid < xtotal) prep_block<FMT, N, XDT>(xraw, X[tid / (N / 16)], tid % (N / 16));
+    if (tid < kPairs) {
+        ids_s[tid] = id_v;
+        rw_s[tid] = rw_v;
+    }
     for (int i = tid + nthreads; i < xtotal; i += nthreads)
         prep_block<FMT, N, XDT>(load_xblock<N, XDT>(xrow_ptr(i), i % (N / 16)), X[i / (N / 16)], i % (N / 16));
     if constexpr (FMT == IQK_IQ1_S_R4) {
@@ -617,13 +644,23 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
     lds_barrier();
 
     const int nunits = u1 - u0;
-    const int my_units = wave < nunits ? (nunits - wave + nwaves - 1) / nwaves : 0;
-    if (my_units == 0) return;
-    const int my_items = my_units * kk;
+    const int nitems = nunits * kk;
+    const int my_items = wave < nitems ? (nitems - wave + nwaves - 1) / nwaves : 0;
+    if constexpr (MODE != kCombine) {
+        if (my_items == 0) return;
+    }
+    const int rem0 = u0 - o_first * p.upo;  // first unit of the block inside its outer
     Cursor lc;  // next item to load
-    lc.outer = (int)fdiv((uint32_t)(u0 + wave), p.dupo);
-    lc.rem = u0 + wave - lc.outer * p.upo;
-    lc.j = 0;
+    if constexpr (MODE == kCombine) {
+        const int ul = (int)fdiv((uint32_t)wave, p.dk);
+        lc.outer = o_first;
+        lc.rem = rem0 + ul;
+        lc.j = wave - ul * p.k;
+    } else {
+        lc.outer = (int)fdiv((uint32_t)(u0 + wave), p.dupo);
+        lc.rem = u0 + wave - lc.outer * p.upo;
+        lc.j = 0;
+    }
     Cursor pc = lc;  // next item to process
 
     constexpr int kHalf = G::RPG / 2;
@@ -633,20 +670,20 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
         if constexpr (MODE == kSwiGLU) return q < kHalf ? rem * kHalf + q : half_out + rem * kHalf + (q - kHalf);
         else return rem * G::RPG + q;
     };
-    auto expert_of = [&](int pair) { return pair == pair_of(o_first, 0) ? id_first : p.ids[pair]; };
+    auto expert_of = [&](int pair) { return __builtin_amdgcn_readfirstlane(ids_s[pair - pr0]); };
 
     // Loads of an item past the wave's last use a zero-record resource.
     auto load_next = [&](Group<FMT, N>& buf, bool live) {
         const ExpertRes res = expert_res<FMT, N>(p, live ? expert_of(pair_of(lc.outer, lc.j)) : -1);
         const int rem = lc.rem;
         load_group<FMT, N>(buf, res, [&](int q) { return unit_row(rem, q); }, lane_row, c);
-        lc.advance(nwaves, p.upo, kk);
+        lc.template advance<MODE>(nwaves, p.upo, p.k);
     };
     // The first two items' rows are requested only now: issued earlier, the
     // launch's row traffic would queue ahead of the activation reads and
     // hold every wave at the barrier until most rows had streamed in.
     Group<FMT, N> bufA, bufB;
-    load_next(bufA, true);
+    load_next(bufA, my_items > 0);
     load_next(bufB, my_items > 1);
 
     uint32_t xh[16], xl[16];
@@ -669,12 +706,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
         cur_x = xi;
     };
 
-    float acc = 0.f;  // kCombine: running sum over the unit's slots
     auto process = [&](const Group<FMT, N>& gb) {
         const int outer = pc.outer;
         const int rem = pc.rem;
         const int j = pc.j;
-        pc.advance(nwaves, p.upo, kk);
+        pc.template advance<MODE>(nwaves, p.upo, p.k);
         const int pair = pair_of(outer, j);
         const bool valid = (unsigned)expert_of(pair) < (unsigned)p.E;
         const int xi = xrow_of(pair) - xr0;
@@ -712,35 +748,49 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
             __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16(hv), hres,
                                                   writer && q < kHalf ? (uint32_t)r * 2u : kOob, 0, 0);
         } else {
-            const float w = j == 0 && outer == o_first ? rw_first : p.rw[pair];
-            const float contrib = w * __uint_as_float(sum);
-            acc = j == 0 ? contrib : acc + contrib;
-            const int r = unit_row(rem, q);
-            const Rsrc yres = make_rsrc(p.y + (int64_t)outer * p.out, (uint32_t)p.out * 4u);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), yres,
-                                                  writer && j == kk - 1 ? (uint32_t)r * 4u : kOob, 0, 0);
+            // slot partial, weighted; summed over the slots in order below
+            const float w = rw_s[pair - pr0];
+            if (writer) part_s[((rem - rem0) * p.k + j) * G::RPG + q] = w * __uint_as_float(sum);
         }
     };
 
     // Items 0 and 1 are in flight.  The loop refills a buffer just before
     // processing the other one, so at its top exactly one item's loads are
     // outstanding on every path and each wait covers only the item it needs.
-    load_x(xrow_of(pair_of(pc.outer, pc.j)) - xr0);
-    process(bufA);
-    if constexpr (FMT == IQK_IQ1_S_R4) {
-        // measured: at one or two items per wave the IQ1_S_R4 instance is
-        // faster without the loop's dead refills (the 2-bit ones are not)
-        if (my_items <= 2) {
-            if (my_items == 2) process(bufB);
-            return;
+    if (MODE != kCombine || my_items > 0) {  // other modes returned above when idle
+        load_x(xrow_of(pair_of(pc.outer, pc.j)) - xr0);
+        process(bufA);
+        bool loop = true;
+        if constexpr (FMT == IQK_IQ1_S_R4) {
+            // measured: at one or two items per wave the IQ1_S_R4 instance is
+            // faster without the loop's dead refills (the 2-bit ones are not)
+            if (my_items <= 2) {
+                if (my_items == 2) process(bufB);
+                loop = false;
+            }
+        }
+        for (int i = 1; loop && i < my_items; i += 2) {
+            load_next(bufA, i + 1 < my_items);
+            process(bufB);
+            load_next(bufB, i + 2 < my_items);
+            if (i + 1 >= my_items) break;
+            process(bufA);
         }
     }
-    for (int i = 1; i < my_items; i += 2) {
-        load_next(bufA, i + 1 < my_items);
-        process(bufB);
-        load_next(bufB, i + 2 < my_items);
-        if (i + 1 >= my_items) break;
-        process(bufA);
+
+    if constexpr (MODE == kCombine) {
+        // y[t, row] = sum over slots in order j = 0..k-1 of the weighted partials
+        lds_barrier();
+        for (int i = tid; i < nunits * G::RPG; i += nthreads) {
+            const int ul = i / G::RPG;
+            const int q = i - ul * G::RPG;
+            const int row = (rem0 + ul) * G::RPG + q;
+            if (row < p.out) {
+                float acc = part_s[(ul * p.k) * G::RPG + q];
+                for (int j = 1; j < p.k; ++j) acc += part_s[(ul * p.k + j) * G::RPG + q];
+                p.y[(int64_t)o_first * p.out + row] = acc;
+            }
+        }
     }
 }
 
@@ -756,8 +806,11 @@ hipError_t launch_inst(GemvParams p, int64_t T, hipStream_t s) {
     if (total <= 0 || total > 0x7FFFFFFF) return hipErrorInvalidValue;
     int64_t nb, bpt = 1;
     if constexpr (MODE == kCombine) {
-        // blocks never straddle tokens: a block holds one token's k activation rows
+        // blocks never straddle tokens (a block holds one token's k
+        // activation rows) and hold at most kCombineMaxUnits units
         bpt = IQK_GEMV_TARGET_BLOCKS / T;
+        const int64_t bpt_lds = (upo + kCombineMaxUnits - 1) / kCombineMaxUnits;
+        bpt = bpt < bpt_lds ? bpt_lds : bpt;
         bpt = bpt < 1 ? 1 : (bpt > upo ? upo : bpt);
         nb = T * bpt;
         p.ubase = (int32_t)(upo / bpt);
@@ -780,7 +833,6 @@ hipError_t launch_inst(GemvParams p, int64_t T, hipStream_t s) {
     int64_t waves = (items + IQK_GEMV_MIN_GROUPS - 1) / IQK_GEMV_MIN_GROUPS;
     waves = items < 4 ? items : ((waves + 3) / 4) * 4;
     waves = waves > kMaxWaves ? kMaxWaves : (waves < 1 ? 1 : waves);
-    if (MODE == kCombine && waves > units) waves = units;  // a unit's slots stay in one wave
     p.outers = (int32_t)outers;
     p.upo = (int32_t)upo;
     p.bpt = (int32_t)bpt;
