@@ -85,6 +85,8 @@ def _load():
         "iqk_grouped_gemm": (i32, [p, i64, i64, i64, p, i32, i64, i32, p, p, p, p]),
         "iqk_moe_prefill_workspace": (i32, [W, i64, i32, p]),
         "iqk_moe_prefill": (i32, [W, p, p, p, i32, p, i64, i32, i32, p, sz, p, p]),
+        "iqk_moe_prefill_fused_workspace": (i32, [W, i64, i32, p]),
+        "iqk_moe_prefill_fused": (i32, [W, p, p, p, i32, p, i64, i32, i32, p, sz, p, p]),
         "iqk_floor_gemv": (i32, [W, p, p, p, i32, i32, p, i64, i32, p, p]),
         "iqk_floor_dequant": (i32, [W, i64, i64, i32, p, p]),
         "iqk_stream_read": (i32, [p, sz, p, sz, p]),
@@ -343,4 +345,32 @@ def moe_prefill(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=None, gri
                                 _dev(ids, "ids", torch.int32), T, k, int(bool(sorted)),
                                 _dev(workspace, "workspace", torch.uint8), workspace.numel(),
                                 _dev(y, "y", torch.float32), _stream(stream)))
+    return y
+
+
+def prefill_fused_workspace_bytes(w: Weights, T: int, k: int) -> int:
+    b = ctypes.c_size_t()
+    cw = _Weights(_fmt(w.fmt), w.experts, w.out, w.in_features, None, 0)
+    _check(_lib.iqk_moe_prefill_fused_workspace(ctypes.byref(cw), T, k, ctypes.byref(b)))
+    return b.value
+
+
+def moe_prefill_fused(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=None, grid: torch.Tensor | None = None,
+                      x_slots: int = 1, sorted: bool = False, workspace: torch.Tensor | None = None,
+                      y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Prefill with the dequantization fused into the MFMA grouped GEMM
+    (route + one kernel; no dense weight copy)."""
+    T, k = ids.shape
+    if x.dtype != torch.bfloat16 or x.numel() != T * x_slots * w.in_features:
+        raise IqkValueError(_E_SIZE, "x must be bf16 [T, x_slots, in]")
+    if workspace is None:
+        workspace = torch.empty(prefill_fused_workspace_bytes(w, T, k), dtype=torch.uint8, device=w.streams.device)
+    if y is None:
+        y = torch.zeros((T, k, w.out), dtype=torch.float32, device=w.streams.device)
+    _v, vp = _host_values(values)
+    cw = w._c()
+    _check(_lib.iqk_moe_prefill_fused(ctypes.byref(cw), vp, _dev(grid, "grid", torch.int8), _dev(x, "x"), x_slots,
+                                      _dev(ids, "ids", torch.int32), T, k, int(bool(sorted)),
+                                      _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                                      _dev(y, "y", torch.float32), _stream(stream)))
     return y

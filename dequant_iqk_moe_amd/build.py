@@ -24,6 +24,7 @@ PER_FILE = {
     "iqk_dequant.hip": ["-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero"],
     "iqk_gemv.hip": [],
     "iqk_prefill.hip": [],
+    "iqk_fused.hip": [],
     "iqk_host.cpp": [],
 }
 

@@ -36,7 +36,7 @@
 // ahead.  One large workgroup per CU (up to 16 waves)
 // amortizes the activation conversion over ~100 rows.  Rows of a workgroup
 // are contiguous, so the small per-row planes share cache lines.
-#include "iqk_internal.h"
+#include "iqk_device.h"
 
 namespace iqk {
 namespace {
@@ -120,42 +120,12 @@ struct Geo {
     static constexpr int RPG = GIT * RPI;                             // rows per reduction group
 };
 
-__device__ __forceinline__ float half_to_float(uint32_t h) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-}
 
 // Workgroup barrier for LDS only: global loads issued before it stay in
 // flight (a full __syncthreads would wait for them).
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-
-// Raw buffer resources.  An access at or past a resource's record count
-// reads zero and a store there is dropped, so every row load and result
-// store below is issued by every lane in every case: work that is absent (a
-// row past the end, a group past the wave's last, an invalid expert id) gets
-// an out-of-range offset or a resource of zero records instead of a branch.
-// With no memory operation behind a branch the compiler counts outstanding
-// loads exactly, and a wave waits for one group of rows while the next group
-// stays in flight.
-using Rsrc = __amdgpu_buffer_rsrc_t;
-constexpr int kRsrcWord3 = 0x00020000;  // raw (unswizzled) buffer, 32-bit data format
-constexpr uint32_t kOob = 0x80000000u;  // an offset past every resource used here
-
-__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
-}
-__device__ __forceinline__ uint4 ld128(Rsrc r, uint32_t off) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
-__device__ __forceinline__ uint2 ld64(Rsrc r, uint32_t off) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-    return make_uint2(v[0], v[1]);
-}
-__device__ __forceinline__ uint32_t ld32(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
-__device__ __forceinline__ uint32_t ld16(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0); }
-__device__ __forceinline__ uint32_t ld8(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0); }
 
 __device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) { return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false); }
 __device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) { return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false); }
@@ -313,82 +283,6 @@ __device__ __forceinline__ void prep_block(const XRaw<XDT>& raw, XLds<N>& L, int
         sum += __shfl_xor(sum, 1);
         if ((b & 1) == 0) L.bsum[b >> 1] = sum;
     }
-}
-
-// Raw stream words of the 64 weights one lane owns in one row.
-struct RowData {
-    uint4 q;  // codes (IQ1_S_R4: q.x, q.y = low index bytes of 8 groups)
-    uint32_t a, b, c, d;
-};
-
-// Byte strides of the planes per row.
-template <int FMT, int N>
-struct Strides {
-    static constexpr int QS = FMT == IQK_IQ1_S_R4 ? N / 8 : N / 4;
-    static constexpr int P1 = FMT == IQK_IQ2_K ? N / 32 : (FMT == IQK_IQ2_KS ? N / 64 : N / 16);
-    static constexpr int P2 = FMT == IQK_IQ2_K ? N / 128 : (FMT == IQK_IQ2_KS ? N / 256 : 2);
-    static constexpr int P3 = FMT == IQK_IQ2_K ? N / 128 : (FMT == IQK_IQ2_KS ? N / 256 : 0);
-    static constexpr int P4 = FMT == IQK_IQ2_KS ? 2 : 0;
-};
-
-// Plane resources of one expert's rows; zero records for an invalid id, so
-// its loads read zeros and move no data.
-struct ExpertRes {
-    Rsrc q, a, b, c, d;
-};
-
-template <int FMT, int N>
-__device__ __forceinline__ ExpertRes expert_res(const GemvParams& p, int e) {
-    using St = Strides<FMT, N>;
-    const bool valid = (unsigned)e < (unsigned)p.E;
-    const int64_t row0 = (int64_t)(valid ? e : 0) * p.out;
-    const uint32_t rows = valid ? (uint32_t)p.out : 0u;
-    const uint8_t* S = p.S;
-    ExpertRes r;
-    r.q = make_rsrc(S + p.off0 + row0 * St::QS, rows * St::QS);
-    r.a = make_rsrc(S + p.off1 + row0 * St::P1, rows * St::P1);
-    if constexpr (FMT == IQK_IQ2_K) {
-        r.b = make_rsrc(S + p.off2 + row0 * St::P2, rows * St::P2);
-        r.d = make_rsrc(S + p.off3 + row0 * St::P3, rows * St::P3);
-        r.c = r.b;
-    } else if constexpr (FMT == IQK_IQ2_KS) {
-        r.b = make_rsrc(S + p.off2 + row0 * St::P2, rows * St::P2);
-        r.c = make_rsrc(S + p.off3 + row0 * St::P3, rows * St::P3);
-        r.d = make_rsrc(S + p.off4 + row0 * 2, rows * 2u);
-    } else {
-        r.d = make_rsrc(S + p.off2 + row0 * 2, rows * 2u);
-        r.b = r.c = r.d;
-    }
-    return r;
-}
-
-// The words one lane needs for expert row `row` (rows at or past `out` are
-// out of range and read zeros).  Resources are uniform, offsets per lane.
-template <int FMT, int N>
-__device__ __forceinline__ RowData load_row(const ExpertRes& x, uint32_t row, uint32_t c) {
-    using St = Strides<FMT, N>;
-    RowData r;
-    if constexpr (FMT == IQK_IQ2_K) {
-        r.q = ld128(x.q, row * St::QS + 16u * c);
-        r.a = ld16(x.a, row * St::P1 + 2u * c);
-        r.b = ld8(x.b, row * St::P2 + (c >> 1));
-        r.c = 0;
-        r.d = ld16(x.d, row * St::P3 + 2u * (c >> 2));
-    } else if constexpr (FMT == IQK_IQ2_KS) {
-        r.q = ld128(x.q, row * St::QS + 16u * c);
-        r.a = ld8(x.a, row * St::P1 + c);
-        r.b = ld8(x.b, row * St::P2 + (c >> 2));
-        r.c = ld8(x.c, row * St::P3 + (c >> 2));
-        r.d = ld16(x.d, row * 2u);
-    } else {
-        const uint2 qq = ld64(x.q, row * St::QS + 8u * c);
-        r.q = make_uint4(qq.x, qq.y, 0, 0);
-        r.a = ld32(x.a, row * St::P1 + 4u * c);
-        r.b = 0;
-        r.c = 0;
-        r.d = ld16(x.d, row * 2u);
-    }
-    return r;
 }
 
 // d = dot4(a, b) with the accumulator starting at zero (VOP3P form with an

@@ -527,6 +527,70 @@ int iqk_moe_prefill(const iqk_weights* w, const float* values, const int8_t* gri
     return ok();
 }
 
+int iqk_moe_prefill_fused_workspace(const iqk_weights* w, int64_t T, int k, size_t* bytes) {
+    if (!w || !bytes) return fail(IQK_E_ARG, "null pointer");
+    int rc = check_fmt_shape(w->fmt, w->in);
+    if (rc) return rc;
+    if (w->experts <= 0 || w->out <= 0 || T < 0 || k <= 0) return fail(IQK_E_ARG, "bad sizes");
+    const int64_t P = T * k;
+    *bytes = round256((size_t)w->experts * 4) + round256((size_t)(w->experts + 1) * 4) +
+             round256((size_t)std::max<int64_t>(P, 1) * 4);
+    return ok();
+}
+
+int iqk_moe_prefill_fused(const iqk_weights* w, const float* values, const int8_t* grid, const void* x_bf16,
+                          int x_slots, const int32_t* ids, int64_t T, int k, int sorted, void* workspace,
+                          size_t ws_bytes, float* y, void* stream) {
+    int rc = check_weights(w);
+    if (rc) return rc;
+    if (w->in != 512 && w->in != 2048 && w->in != 4096)
+        return fail(IQK_E_WIDTH, "fused prefill has no instance for input width %lld (instances: 512, 2048, 4096)",
+                    (long long)w->in);
+    if (T < 0 || k <= 0) return fail(IQK_E_ARG, "T must be >= 0 and k > 0");
+    if (T * k > (1LL << 24)) return fail(IQK_E_ARG, "too many pairs");
+    if (x_slots != 1 && x_slots != k) return fail(IQK_E_ARG, "x_slots must be 1 or k");
+    if (sorted != 0 && sorted != 1) return fail(IQK_E_ARG, "sorted must be 0 or 1");
+    if (w->experts > 16384) return fail(IQK_E_ARG, "prefill routing supports at most 16384 experts");
+    if (w->out * (int64_t)iqk::row_bytes(w->fmt, w->in) > 0x7FFFFFFFLL)
+        return fail(IQK_E_ARG, "fused prefill needs out * row bytes < 2^31 (out = %lld)", (long long)w->out);
+    if (w->fmt == IQK_IQ1_S_R4 ? !grid : !values) return fail(IQK_E_ARG, "missing value table or grid");
+    size_t need = 0;
+    rc = iqk_moe_prefill_fused_workspace(w, T, k, &need);
+    if (rc) return rc;
+    if (!workspace || ws_bytes < need) return fail(IQK_E_SIZE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+    if (T > 0 && (!x_bf16 || !ids || !y)) return fail(IQK_E_ARG, "null x, ids or output");
+    if (T == 0) return ok();
+    const int64_t E = w->experts, P = T * k;
+    uint8_t* ws = (uint8_t*)workspace;
+    int32_t* counts = (int32_t*)ws;
+    ws += round256((size_t)E * 4);
+    int32_t* offsets = (int32_t*)ws;
+    ws += round256((size_t)(E + 1) * 4);
+    int32_t* perm = (int32_t*)ws;
+    hipStream_t s = (hipStream_t)stream;
+    iqk::RouteLaunch RL{ids, P, E, sorted, counts, offsets, perm};
+    hipError_t e = iqk::launch_route(RL, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill route launch");
+    iqk::FusedLaunch FL;
+    FL.fmt = w->fmt;
+    FL.E = E;
+    FL.out = w->out;
+    FL.n = w->in;
+    FL.streams = (const uint8_t*)w->streams;
+    FL.pl = iqk::planes(w->fmt, E * w->out, w->in);
+    FL.values = values;
+    FL.grid = grid;
+    FL.x = x_bf16;
+    FL.x_slots = x_slots;
+    FL.k = k;
+    FL.offsets = offsets;
+    FL.perm = perm;
+    FL.y = y;
+    e = iqk::launch_fused_prefill(FL, s);
+    if (e != hipSuccess) return hip_fail(e, "fused prefill launch");
+    return ok();
+}
+
 int iqk_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, void* stream) {
     if (!buf || !sink || bytes == 0 || bytes % 16 || sink_words == 0) return fail(IQK_E_ARG, "bad stream-read arguments");
     hipError_t e = iqk::launch_stream_read(buf, bytes, sink, sink_words, (hipStream_t)stream);

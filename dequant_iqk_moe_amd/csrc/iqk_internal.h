@@ -103,7 +103,21 @@ struct GemmLaunch {
     float* y;
 };
 
+struct FusedLaunch {
+    int fmt;
+    int64_t E, out, n;
+    const uint8_t* streams;
+    Planes pl;
+    const float* values;  // host float[8] (2-bit members)
+    const int8_t* grid;   // device int8[2048 * 8] (IQ1_S_R4)
+    const void* x;        // bf16 [T, x_slots, n]
+    int x_slots, k;
+    const int32_t *offsets, *perm;
+    float* y;
+};
+
 hipError_t launch_dequant(const DequantLaunch& a, bool floor_variant, hipStream_t s);
+hipError_t launch_fused_prefill(const FusedLaunch& a, hipStream_t s);
 hipError_t launch_gemv(const GemvLaunch& a, bool floor_variant, hipStream_t s);
 hipError_t launch_route(const RouteLaunch& a, hipStream_t s);
 hipError_t launch_grouped_gemm(const GemmLaunch& a, hipStream_t s);

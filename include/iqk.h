@@ -192,6 +192,25 @@ int iqk_grouped_gemm(const void* W_bf16, int64_t E, int64_t out, int64_t in,
                      const void* x_bf16, int x_slots, int64_t T, int k,
                      const int32_t* offsets, const int32_t* perm, float* y, void* stream);
 
+/* Workspace of iqk_moe_prefill_fused: the routing arrays only (counts,
+ * offsets, permutation), each rounded up to 256 bytes. */
+int iqk_moe_prefill_fused_workspace(const iqk_weights* w, int64_t T, int k, size_t* bytes);
+
+/* Prefill with the dequantization fused into the MFMA grouped GEMM (the
+ * two passes of "Surface" -- dequantize the stacked experts, then the
+ * grouped GEMM -- in one kernel, without the dense copy): iqk_route, then
+ * per expert the same bf16 weights iqk_dequant would write, rebuilt from
+ * the compressed streams in registers and multiplied with the expert's
+ * gathered bf16 token rows, float32 accumulation.  Arguments as
+ * iqk_moe_prefill (workspace from iqk_moe_prefill_fused_workspace); the
+ * value table may be any float32 values.  Widths: in = 512, 2048 or 4096
+ * (IQK_E_WIDTH otherwise); out * iqk_row_bytes(fmt, in) < 2^31.
+ * Accuracy: as iqk_moe_prefill (2e-2 against the float32-weight product;
+ * the result differs from iqk_moe_prefill only in summation order). */
+int iqk_moe_prefill_fused(const iqk_weights* w, const float* values, const int8_t* grid,
+                          const void* x_bf16, int x_slots, const int32_t* ids, int64_t T, int k,
+                          int sorted, void* workspace, size_t ws_bytes, float* y, void* stream);
+
 /* Workspace of iqk_moe_prefill: the dense bf16 copy of all experts plus the
  * routing arrays, each rounded up to 256 bytes. */
 int iqk_moe_prefill_workspace(const iqk_weights* w, int64_t T, int k, size_t* bytes);
