@@ -25,10 +25,12 @@
 //     v_perm_b32 of doubled code bytes.  About 2-3 VALU instructions per
 //     weight, once per weight whatever the number of tokens.
 //   * The expert's token rows (gathered through the routing permutation)
-//     are staged in LDS, 2048 k at a time for up to 32 tokens, already in
+//     are staged in LDS (all of k for up to 16 tokens, 2048 k at a time for
+//     up to 32), already in
 //     the k order the fragments use (a per-step permutation that makes both
 //     the table lookups and the LDS reads 16-byte contiguous); rows are
-//     padded by 16 bytes so a fragment read is bank-conflict free.
+//     padded by 32 bytes against bank conflicts.  Each lane keeps the raw
+//     words of the next four k steps in flight.
 //   * Results go straight to y[t, j, :] (no scatter pass).
 #include "iqk_device.h"
 
@@ -41,12 +43,22 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kFWaves = 16;                 // waves per block, one 16-row tile each
+#ifndef IQK_FUSED_WAVES
+#define IQK_FUSED_WAVES 16
+#endif
+constexpr int kFWaves = IQK_FUSED_WAVES;    // waves per block, one 16-row tile each
 constexpr int kFThreads = 64 * kFWaves;
 constexpr int kFRows = 16 * kFWaves;        // weight rows per block
 constexpr int kFMT = 2;                     // 16-token tiles per pass over k
-constexpr int kFKChunk = 2048;              // activation k staged in LDS at a time
-constexpr int kFRowBytes = 2 * kFKChunk + 16;  // LDS row pitch (padding: conflict-free reads)
+constexpr int kFPad = 32;                   // LDS row padding (bank-conflict-free fragment reads)
+// LDS for the staged token rows: one tile over all k up to 4096, or two
+// tiles over 2048 k at a time
+#ifndef IQK_FUSED_KC1
+#define IQK_FUSED_KC1 4096  // k staged at a time for one token tile
+#endif
+constexpr int kFKC1 = IQK_FUSED_KC1;
+constexpr int kFStageBytes = 32 * (2 * 2048 + kFPad) > 16 * (2 * kFKC1 + kFPad) ? 32 * (2 * 2048 + kFPad)
+                                                                                : 16 * (2 * kFKC1 + kFPad);
 
 struct FusedParams {
     const uint8_t* S;
@@ -59,6 +71,8 @@ struct FusedParams {
     const int32_t* offsets;  // [E + 1]
     const int32_t* perm;     // expert-sorted pair indices
     float* y;                // [T * k, out]
+    int64_t y_bytes;
+    const int64_t* plan;     // [E + 1] cost prefix (work plan)
 };
 
 // Workgroup barrier for LDS only: global loads issued before it stay in
@@ -72,65 +86,81 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Two bf16 weights from a 4-entry table (entries 0..3 at bytes 2c, 2c+1 of
-// tlo:thi): `d2` holds 2 * code in its bytes, `d2p1` 2 * code + 1, and
-// `sel` picks which two code bytes form the pair.
-__device__ __forceinline__ uint32_t table_pair(uint32_t tlo, uint32_t thi, uint32_t d2, uint32_t d2p1, uint32_t sel) {
-    return __builtin_amdgcn_perm(thi, tlo, __builtin_amdgcn_perm(d2p1, d2, sel));
-}
-
-// Fragment selectors: bytes (x, y) of the code word give the pair
-// [2 c_x, 2 c_x + 1, 2 c_y, 2 c_y + 1] (byte 4 + i of the perm source is
-// byte i of d2p1).
-constexpr uint32_t sel_pair(int x, int y) {
-    return (uint32_t)x | (uint32_t)(4 + x) << 8 | (uint32_t)y << 16 | (uint32_t)(4 + y) << 24;
-}
-
-// 4-entry bf16 table of one sub-block: values v0..v3.
+// 4-entry bf16 table of one sub-block, split by byte: `lo` holds the low
+// bytes of the four values, `hi` the high bytes.  A pair of weights with
+// codes (a, b) is then perm(hi, lo, [a, 4 + a, b, 4 + b]).
 struct Tab {
     uint32_t lo, hi;
 };
 __device__ __forceinline__ Tab make_tab(float v0, float v1, float v2, float v3) {
-    return Tab{pk_bf16(v0, v1), pk_bf16(v2, v3)};
+    const uint32_t p0 = pk_bf16(v0, v1), p1 = pk_bf16(v2, v3);
+    return Tab{__builtin_amdgcn_perm(p1, p0, 0x06040200u), __builtin_amdgcn_perm(p1, p0, 0x07050301u)};
 }
 
-// The eight B fragments (4 dwords each) of one lane's 64-weight chunk.
+// Selector [c_x, 4 + c_x, c_y, 4 + c_y] from code bytes x, y of v (v4 = v + 4
+// in every byte; byte 4 + i of the perm source is byte i of v4).
+constexpr uint32_t sel_pair(int x, int y) {
+    return (uint32_t)x | (uint32_t)(4 + x) << 8 | (uint32_t)y << 16 | (uint32_t)(4 + y) << 24;
+}
+__device__ __forceinline__ uint32_t table_pair(const Tab& t, uint32_t v, uint32_t v4, uint32_t sel) {
+    return __builtin_amdgcn_perm(t.hi, t.lo, __builtin_amdgcn_perm(v4, v, sel));
+}
+
+// The value table in vector registers, as named members: an array here
+// would be turned into a private-memory lookup by the alphabet select.
+struct Table8 {
+    float v0, v1, v2, v3, v4, v5, v6, v7;
+};
+
+// The eight B fragments (4 dwords each) of one lane's 64-weight chunk, each
+// handed to emit(fragment index, fragment) as soon as it is built.
 // 2-bit members: fragment 2i + h holds weights (4h + d, 4h + d + 8) of code
 // word i as dword d; IQ1_S_R4: fragment 2b + j holds group j of block b in
 // natural order.
-template <int FMT>
-__device__ __forceinline__ void decode_chunk(const RowData& r, int c, const float* tab, const uint2* grid_s,
-                                             u32x4 (&B)[8]) {
+template <int FMT, class Emit>
+__device__ __forceinline__ void decode_chunk(const RowData& r, int c, const Table8& tv, const uint2* grid_s,
+                                             Emit emit) {
     const float d = half_to_float(r.d);
     if constexpr (FMT == IQK_IQ2_K || FMT == IQK_IQ2_KS) {
         const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
         Tab t{0u, 0u};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            int si;
-            uint32_t alpha;
-            if constexpr (FMT == IQK_IQ2_K) {
-                si = __builtin_amdgcn_sbfe((int)(r.a ^ 0x8888u), 4 * i, 4);  // nibble - 8
-                alpha = (r.b >> (4 * (c & 1) + i)) & 1u;
-            } else {
-                const int j = i >> 1;  // 32-weight sub-block
-                const int sh = 2 * (c & 3) + j;
-                si = (int)(((r.a >> (4 * j)) & 15u) | (((r.b >> sh) & 1u) << 4)) - 16;
-                alpha = (r.c >> sh) & 1u;
-            }
             if (FMT == IQK_IQ2_K || (i & 1) == 0) {  // IQ2_KS: one table per two code words
+                int si;
+                bool alpha;
+                if constexpr (FMT == IQK_IQ2_K) {
+                    si = __builtin_amdgcn_sbfe((int)(r.a ^ 0x8888u), 4 * i, 4);  // nibble - 8
+                    alpha = (r.b >> (4 * (c & 1) + i)) & 1u;
+                } else {
+                    const int j = i >> 1;  // 32-weight sub-block
+                    const int sh = 2 * (c & 3) + j;
+                    si = (int)(((r.a >> (4 * j)) & 15u) | (((r.b >> sh) & 1u) << 4)) - 16;
+                    alpha = (r.c >> sh) & 1u;
+                }
                 const float s = d * (float)si;
-                t = alpha ? make_tab(s * tab[4], s * tab[5], s * tab[6], s * tab[7])
-                          : make_tab(s * tab[0], s * tab[1], s * tab[2], s * tab[3]);
+                // alphabet select as one v_bfi_b32 per value (written as C the
+                // compiler makes it two instructions, or a private-memory lookup)
+                const uint32_t m = 0u - (uint32_t)alpha;
+                auto pick = [&](float lo, float hi) {
+                    float r;
+                    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(hi), "v"(lo));
+                    return r;
+                };
+                t = make_tab(s * pick(tv.v0, tv.v4), s * pick(tv.v1, tv.v5), s * pick(tv.v2, tv.v6),
+                             s * pick(tv.v3, tv.v7));
             }
+            u32x4 f0, f1;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 // bytes of v: codes of weights jj, 4 + jj, 8 + jj, 12 + jj
                 const uint32_t v = (q[i] >> (2 * jj)) & 0x03030303u;
-                const uint32_t d2 = v + v, d2p1 = d2 + 0x01010101u;
-                B[2 * i][jj] = table_pair(t.lo, t.hi, d2, d2p1, sel_pair(0, 2));      // (jj, 8 + jj)
-                B[2 * i + 1][jj] = table_pair(t.lo, t.hi, d2, d2p1, sel_pair(1, 3));  // (4 + jj, 12 + jj)
+                const uint32_t v4 = v + 0x04040404u;
+                f0[jj] = table_pair(t, v, v4, sel_pair(0, 2));  // (jj, 8 + jj)
+                f1[jj] = table_pair(t, v, v4, sel_pair(1, 3));  // (4 + jj, 12 + jj)
             }
+            emit(2 * i, f0);
+            emit(2 * i + 1, f1);
         }
     } else {
 #pragma unroll
@@ -146,148 +176,406 @@ __device__ __forceinline__ void decode_chunk(const RowData& r, int c, const floa
                 const uint32_t idx = ((qsw >> (8 * j)) & 0xFFu) | (((h16 >> (3 * j)) & 7u) << 8);
                 const uint2 gv = grid_s[idx];
                 const uint32_t v0 = gv.x & 0x03030303u, v1 = gv.y & 0x03030303u;
-                const uint32_t a2 = v0 + v0, a2p1 = a2 + 0x01010101u;
-                const uint32_t b2 = v1 + v1, b2p1 = b2 + 0x01010101u;
-                B[4 * b + j][0] = table_pair(t.lo, t.hi, a2, a2p1, sel_pair(0, 1));
-                B[4 * b + j][1] = table_pair(t.lo, t.hi, a2, a2p1, sel_pair(2, 3));
-                B[4 * b + j][2] = table_pair(t.lo, t.hi, b2, b2p1, sel_pair(0, 1));
-                B[4 * b + j][3] = table_pair(t.lo, t.hi, b2, b2p1, sel_pair(2, 3));
+                const uint32_t v04 = v0 + 0x04040404u, v14 = v1 + 0x04040404u;
+                u32x4 f;
+                f[0] = table_pair(t, v0, v04, sel_pair(0, 1));
+                f[1] = table_pair(t, v0, v04, sel_pair(2, 3));
+                f[2] = table_pair(t, v1, v14, sel_pair(0, 1));
+                f[3] = table_pair(t, v1, v14, sel_pair(2, 3));
+                emit(4 * b + j, f);
             }
         }
     }
 }
 
-// Logical k (inside a 256-wide step) of fragment slot pp = (mi * 4 + g) * 8 + e
-// of MFMA mi, lane group g, element e: the k order both operands share.
-template <int FMT>
-__device__ __forceinline__ int slot_k(int mi, int g, int e) {
-    if constexpr (FMT == IQK_IQ1_S_R4) return 64 * g + 8 * mi + e;
-    return 64 * g + 16 * (mi >> 1) + 4 * (mi & 1) + (e >> 1) + 8 * (e & 1);
+// Raw words of two adjacent 64-weight chunks c0, c0 + 1 (c0 even) of one
+// row: the four lanes of a row then read its codes as one 128-byte line per
+// 512 k instead of two half lines.
+struct RowPair {
+    uint4 q0, q1;
+    uint32_t a, a2, b, c, d;
+};
+
+template <int FMT, int N>
+__device__ __forceinline__ RowPair load_pair(const ExpertRes& x, uint32_t row, uint32_t c0) {
+    using St = Strides<FMT, N>;
+    RowPair r;
+    r.a2 = r.c = 0;
+    if constexpr (FMT == IQK_IQ2_K) {
+        r.q0 = ld128(x.q, row * St::QS + 16u * c0);
+        r.q1 = ld128(x.q, row * St::QS + 16u * c0 + 16u);
+        r.a = ld32(x.a, row * St::P1 + 2u * c0);          // 4 scale nibbles per chunk
+        r.b = ld8(x.b, row * St::P2 + (c0 >> 1));          // alphabet bits of both chunks
+        r.d = ld16(x.d, row * St::P3 + 2u * (c0 >> 2));    // both chunks in one super-block
+    } else if constexpr (FMT == IQK_IQ2_KS) {
+        r.q0 = ld128(x.q, row * St::QS + 16u * c0);
+        r.q1 = ld128(x.q, row * St::QS + 16u * c0 + 16u);
+        r.a = ld16(x.a, row * St::P1 + c0);
+        r.b = ld8(x.b, row * St::P2 + (c0 >> 2));
+        r.c = ld8(x.c, row * St::P3 + (c0 >> 2));
+        r.d = ld16(x.d, row * 2u);
+    } else {
+        const uint4 qq = ld128(x.q, row * St::QS + 8u * c0);
+        r.q0 = make_uint4(qq.x, qq.y, 0u, 0u);
+        r.q1 = make_uint4(qq.z, qq.w, 0u, 0u);
+        const uint2 h = ld64(x.a, row * St::P1 + 4u * c0);
+        r.a = h.x;
+        r.a2 = h.y;
+        r.b = 0;
+        r.d = ld16(x.d, row * 2u);
+    }
+    return r;
+}
+
+// The words of chunk c0 + H of a pair in the single-chunk form.
+template <int FMT, int H>
+__device__ __forceinline__ RowData half_of(const RowPair& r) {
+    RowData o;
+    o.q = H ? r.q1 : r.q0;
+    if constexpr (FMT == IQK_IQ2_K) o.a = H ? r.a >> 16 : r.a & 0xFFFFu;
+    else if constexpr (FMT == IQK_IQ2_KS) o.a = H ? r.a >> 8 : r.a & 0xFFu;
+    else o.a = H ? r.a2 : r.a;
+    o.b = r.b;
+    o.c = r.c;
+    o.d = r.d;
+    return o;
+}
+
+template <int FMT, int N>
+struct FusedShared {
+    __attribute__((aligned(16))) uint8_t A[kFStageBytes];  // token rows, fragment k order
+    uint2 grid[FMT == IQK_IQ1_S_R4 ? 2048 : 1];
+    float tab[8];
+    int64_t xoff[16 * kFMT];  // element offset of each staged token row in x (-1: none)
+};
+
+// Fragment order of the staged token rows.  A super-step covers 512 k; lane
+// group g owns chunks 2g and 2g + 1 of it (logical k 128 g .. 128 g + 127),
+// and its step h (0, 1) uses chunk 2g + h.  Slot (h, mi, g, e) -- MFMA mi of
+// step h, lane group g, element e -- sits at ((h * 8 + mi) * 4 + g) * 8 + e
+// and holds logical k 128 g + 64 h + w(mi, e), w the within-chunk order of
+// the fragment build (2-bit members: 16 (mi / 2) + 4 (mi % 2) + e / 2 +
+// 8 (e % 2); IQ1_S_R4: 8 mi + e).
+
+// Stage token rows tb .. tb + 16 MT of the expert (zeros past M) for k in
+// [kc, kc + KC) into LDS in fragment order.  One unit = 16 logical k of one
+// token row = two 16-byte slots; the loop is unrolled so every thread's
+// loads are in flight together.  Row offsets come from sh.xoff.
+template <int FMT, int N, int MT, int KC>
+__device__ __forceinline__ void stage_tokens(const FusedParams& p, FusedShared<FMT, N>& sh, int kc, int tid) {
+    constexpr int PITCH = 2 * KC + kFPad;
+    constexpr int UNITS = 16 * MT * (KC / 16);
+    constexpr int UPT = (UNITS + kFThreads - 1) / kFThreads;
+#pragma unroll
+    for (int it = 0; it < UPT; ++it) {
+        const int u = tid + it * kFThreads;
+        if (UNITS % kFThreads != 0 && u >= UNITS) break;
+        const int r = u / (KC / 16);
+        const int lu = u - r * (KC / 16);
+        const int64_t xo = sh.xoff[r];
+        uint32_t in[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        if (xo >= 0) {
+            const uint4* src = (const uint4*)(p.x + xo + kc + 16 * lu);
+            const uint4 a = src[0], b = src[1];
+            in[0] = a.x; in[1] = a.y; in[2] = a.z; in[3] = a.w;
+            in[4] = b.x; in[5] = b.y; in[6] = b.z; in[7] = b.w;
+        }
+        const int L = (16 * lu) & 511;  // logical k inside the super-step
+        const int sstep = (16 * lu) >> 9;
+        const int gg = L >> 7;
+        const int hh = (L >> 6) & 1;
+        uint8_t* rowp = sh.A + r * PITCH + sstep * 1024;
+        if constexpr (FMT == IQK_IQ1_S_R4) {
+            const int mi = (L & 63) >> 3;  // two consecutive 8-weight groups
+            *(uint4*)(rowp + (((hh * 8 + mi) * 4 + gg) * 8) * 2) = make_uint4(in[0], in[1], in[2], in[3]);
+            *(uint4*)(rowp + (((hh * 8 + mi + 1) * 4 + gg) * 8) * 2) = make_uint4(in[4], in[5], in[6], in[7]);
+        } else {
+            const int i = (L & 63) >> 4;  // code word of the chunk
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t o[4];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    // (L[4h + d], L[4h + d + 8]) from dwords holding (L[2w], L[2w + 1])
+                    const int x = 4 * h + d;
+                    o[d] = __builtin_amdgcn_perm(in[(x + 8) >> 1], in[x >> 1], (x & 1) ? 0x07060302u : 0x05040100u);
+                }
+                *(uint4*)(rowp + (((hh * 8 + 2 * i + h) * 4 + gg) * 8) * 2) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+    }
+}
+
+// Token tiles tb .. tb + 16 * MT of the expert against its row blocks
+// rb0 .. rb1 - 1 (256 rows each; wave w owns rows 16 w .. 16 w + 15 of a
+// block).  When all of k fits in LDS (one tile, or a short k) the tokens
+// are staged once and the raw-word stream runs on from one row block into
+// the next; otherwise each row block re-stages them 2048 k at a time.
+template <int FMT, int N, int MT>
+__device__ __forceinline__ void fused_pass(const FusedParams& p, FusedShared<FMT, N>& sh, const ExpertRes& res,
+                                           const Table8& tv, int base, int M, int tb,
+                                           int rb0, int rb1, int tid, int li, int g, int wave) {
+    constexpr int KC = MT == 1 ? (N < kFKC1 ? N : kFKC1) : (N < 2048 ? N : 2048);
+    constexpr int PITCH = 2 * KC + kFPad;  // LDS row pitch
+    constexpr int SSC = KC / 512;          // super-steps per chunk
+    // super-steps in flight (IQ2_KS: one, since two spill at k = 4096)
+    constexpr int DW = FMT == IQK_IQ2_KS ? 1 : 2;
+    constexpr int D = SSC < DW ? SSC : DW;
+    constexpr bool WHOLE = KC == N;
+    static_assert(MT * 16 * PITCH <= kFStageBytes && SSC % D == 0 && KC % 512 == 0, "staging layout");
+    auto row_of = [&](int rb) __attribute__((always_inline)) { return rb * kFRows + wave * 16 + li; };
+    const Rsrc yres = make_rsrc(p.y, (uint32_t)p.y_bytes);
+
+    // D[token 4 g + i][weight row li] of each tile; absent tokens and rows
+    // past `out` go to an out-of-range offset
+    auto store = [&](const f32x4 (&acc)[MT], int row) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ti = tb + 16 * m + 4 * g + i;
+                const bool ok = ti < M && row < p.out;
+                const int pr = p.perm[base + (ok ? ti : 0)];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[m][i]), yres,
+                                                      ok ? (uint32_t)((pr * p.out + row) * 4) : kOob, 0, 0);
+            }
+        }
+    };
+    auto mma_step = [&](f32x4 (&acc)[MT], const RowPair& rp, int c0, int sstep) __attribute__((always_inline)) {
+        const uint8_t* arow = sh.A + li * PITCH + sstep * 1024 + g * 16;
+        auto mma = [&](const uint8_t* ar, int mi, const u32x4& b) __attribute__((always_inline)) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const u32x4 a = *(const u32x4*)(ar + m * 16 * PITCH + mi * 64);
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                 __builtin_bit_cast(bf16x8, b), acc[m], 0, 0, 0);
+            }
+        };
+        decode_chunk<FMT>(half_of<FMT, 0>(rp), c0, tv, sh.grid, [&](int mi, const u32x4& b) __attribute__((always_inline)) { mma(arow, mi, b); });
+        // IQ1_S_R4: keep the scheduler from hoisting the second half's grid
+        // and activation reads over the first half (it runs out of registers)
+        if constexpr (FMT == IQK_IQ1_S_R4 && N != 4096) __builtin_amdgcn_sched_barrier(0);
+        decode_chunk<FMT>(half_of<FMT, 1>(rp), c0 + 1, tv, sh.grid,
+                          [&](int mi, const u32x4& b) __attribute__((always_inline)) { mma(arow + 512, mi, b); });
+    };
+    auto write_xoff = [&]() __attribute__((always_inline)) {
+        // the staged rows' activation offsets (the routing lookups once per row)
+        if (tid < 16 * MT) {
+            const int ti = tb + tid;
+            int64_t off = -1;
+            if (ti < M) {
+                const int pair = p.perm[base + ti];
+                const int t = pair / p.k;
+                const int sl = p.x_slots == 1 ? 0 : pair - t * p.k;
+                off = ((int64_t)t * p.x_slots + sl) * N;
+            }
+            sh.xoff[tid] = off;
+        }
+    };
+
+    if constexpr (WHOLE) {
+        RowPair buf[D];
+#pragma unroll
+        for (int u = 0; u < D; ++u) buf[u] = load_pair<FMT, N>(res, (uint32_t)row_of(rb0), (uint32_t)(8 * u + 2 * g));
+        write_xoff();
+        lds_barrier();  // offsets written; the previous pass's fragments are read
+        stage_tokens<FMT, N, MT, KC>(p, sh, 0, tid);
+        lds_barrier();
+#pragma unroll 1
+        for (int rb = rb0; rb < rb1; ++rb) {
+            f32x4 acc[MT];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+            for (int ss = 0; ss < SSC; ss += D) {
+#pragma unroll
+                for (int u = 0; u < D; ++u) {
+                    mma_step(acc, buf[u], 8 * (ss + u) + 2 * g, ss + u);
+                    // refill D super-steps ahead, running on into the next row block
+                    const bool wrap = ss + u + D >= SSC;
+                    const int nrb = wrap ? rb + 1 : rb;
+                    const int nss = wrap ? ss + u + D - SSC : ss + u + D;
+                    // (past the block's last row block: row `out`, out of range, reads zeros)
+                    buf[u] = load_pair<FMT, N>(res, (uint32_t)(nrb < rb1 ? row_of(nrb) : p.out),
+                                               (uint32_t)(8 * nss + 2 * g));
+                }
+            }
+            store(acc, row_of(rb));
+        }
+    } else {
+        write_xoff();
+#pragma unroll 1
+        for (int rb = rb0; rb < rb1; ++rb) {
+            const int row = row_of(rb);
+            f32x4 acc[MT];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kc = 0; kc < N; kc += KC) {
+                // raw words of the chunk's first D super-steps, in flight during the staging
+                RowPair buf[D];
+#pragma unroll
+                for (int u = 0; u < D; ++u)
+                    buf[u] = load_pair<FMT, N>(res, (uint32_t)row, (uint32_t)(kc / 64 + 8 * u + 2 * g));
+                lds_barrier();  // the previous chunk's fragments are read
+                stage_tokens<FMT, N, MT, KC>(p, sh, kc, tid);
+                lds_barrier();
+#pragma unroll 1
+                for (int ss = 0; ss < SSC; ss += D) {
+#pragma unroll
+                    for (int u = 0; u < D; ++u) {
+                        const int c0 = kc / 64 + 8 * (ss + u) + 2 * g;
+                        mma_step(acc, buf[u], c0, ss + u);
+                        buf[u] = load_pair<FMT, N>(res, (uint32_t)(ss + u + D < SSC ? row : p.out),
+                                                   (uint32_t)(c0 + 8 * D));
+                    }
+                }
+            }
+            store(acc, row);
+        }
+    }
+}
+
+// Work plan.  The kernel's work is split into units of one 256-row block of
+// one expert; a unit's cost is the sum over the expert's token tiles of the
+// measured cost of one pass (decode of the block's weights plus the MFMA
+// work of 16 or 32 tokens; a 32-token pass over a 4096-wide row also
+// re-stages its tokens per row block).  plan[e] is the cost of all units of
+// experts before e; block b of G takes the units whose cost range starts in
+// [b C / G, (b + 1) C / G), C = plan[E], so heavy experts are spread over
+// more blocks and each block walks a contiguous run of row blocks.
+template <int N>
+__device__ __forceinline__ int64_t rb_cost(int M) {
+    constexpr int C1 = 7;                  // one 16-token pass
+    constexpr int C2 = N > 2048 ? 12 : 10;  // one 32-token pass
+    const int full = M / 32, r = M - 32 * full;
+    return (int64_t)full * C2 + (r > 16 ? C2 : (r > 0 ? C1 : 0));
+}
+
+template <int N>
+__global__ __launch_bounds__(kFThreads) void fused_plan_kernel(const int32_t* offsets, int E, int nrb, int64_t* plan) {
+    __shared__ int64_t part[kFThreads];
+    const int tid = threadIdx.x;
+    int64_t carry = 0;
+    if (tid == 0) plan[0] = 0;
+    for (int c = 0; c < E; c += kFThreads) {
+        const int e = c + tid;
+        const int64_t v = e < E ? rb_cost<N>(offsets[e + 1] - offsets[e]) * nrb : 0;
+        part[tid] = v;
+        __syncthreads();
+        // inclusive scan (Hillis-Steele) over the chunk
+        for (int o = 1; o < kFThreads; o <<= 1) {
+            const int64_t add = tid >= o ? part[tid - o] : 0;
+            __syncthreads();
+            part[tid] += add;
+            __syncthreads();
+        }
+        if (e < E) plan[e + 1] = carry + part[tid];
+        carry += part[kFThreads - 1];
+        __syncthreads();
+    }
 }
 
 template <int FMT, int N>
 __global__ __launch_bounds__(kFThreads) void fused_prefill_kernel(FusedParams p) {
-    constexpr int KC = N < kFKChunk ? N : kFKChunk;
-    __shared__ __attribute__((aligned(16))) uint8_t A_s[kFMT * 16 * kFRowBytes];
-    __shared__ uint2 grid_s[FMT == IQK_IQ1_S_R4 ? 2048 : 1];
+    __shared__ FusedShared<FMT, N> sh;
+    __shared__ int e_first;
+    __shared__ uint64_t cand;            // experts e0 .. e0 + 63 with units in this block
+    __shared__ int cand_rb[64][2];
+    __shared__ int more;
 
-    const int e = blockIdx.y;
-    const int base = p.offsets[e];
-    const int M = p.offsets[e + 1] - base;
-    if (M <= 0) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int li = lane & 15;  // weight row of the tile (B) / token of the tile (A)
-    const int g = lane >> 4;   // lane group: 64-weight chunk of the step
-    const int row = blockIdx.x * kFRows + wave * 16 + li;  // rows past `out` read zeros
-    const ExpertRes res = expert_res<FMT, N>(p, e);
-    const ExpertRes none = expert_res<FMT, N>(p, -1);  // zero records: reads nothing
+    const int g = lane >> 4;   // lane group: 128-weight span of the super-step
+    const int nrb = (p.out + kFRows - 1) / kFRows;
+    const int64_t C = p.plan[p.E];
+    const int64_t lo = C * blockIdx.x / gridDim.x, hi = C * (blockIdx.x + 1) / gridDim.x;
+    if (lo >= hi) return;
 
     if constexpr (FMT == IQK_IQ1_S_R4) {
-        ((uint4*)grid_s)[tid] = ((const uint4*)p.grid)[tid];  // 1024 x 16 bytes
+        for (int i = tid; i < 1024; i += kFThreads) ((uint4*)sh.grid)[i] = ((const uint4*)p.grid)[i];
     }
+    if (tid < 8) sh.tab[tid] = p.tab[tid];
+    // the expert whose cost range holds lo (exactly one: plan is non-decreasing, plan[0] = 0 <= lo < C)
+    for (int e = tid; e < p.E; e += kFThreads)
+        if (p.plan[e] <= lo && p.plan[e + 1] > lo) e_first = e;
+    __syncthreads();
+    // the value table in vector registers (the alphabet select needs them there)
+    const Table8 tv{sh.tab[0], sh.tab[1], sh.tab[2], sh.tab[3], sh.tab[4], sh.tab[5], sh.tab[6], sh.tab[7]};
 
-    for (int tb = 0; tb < M; tb += 16 * kFMT) {
-        const int mtc = M - tb > 16 ? 2 : 1;  // token tiles in this pass
-        f32x4 acc[kFMT];
-#pragma unroll
-        for (int m = 0; m < kFMT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        for (int kc = 0; kc < N; kc += KC) {
-            // this lane's first raw words of the chunk, in flight during the staging
-            RowData cur = load_row<FMT, N>(res, (uint32_t)row, (uint32_t)(kc / 64 + g));
-            lds_barrier();  // the previous chunk's fragments are read
-            // Stage tokens tb .. tb + 32 (zeros past M) for k in [kc, kc + KC):
-            // one unit = 16 logical k of one token row = two 16-byte slots.
-            for (int u = tid; u < 16 * kFMT * (KC / 16); u += kFThreads) {
-                const int r = u / (KC / 16);
-                const int lu = u - r * (KC / 16);
-                const int ti = tb + r;
-                uint32_t in[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-                if (ti < M) {
-                    const int pair = p.perm[base + ti];
-                    const int t = pair / p.k;
-                    const int sl = p.x_slots == 1 ? 0 : pair - t * p.k;
-                    const uint4* src = (const uint4*)(p.x + ((int64_t)t * p.x_slots + sl) * N + kc + 16 * lu);
-                    const uint4 a = src[0], b = src[1];
-                    in[0] = a.x; in[1] = a.y; in[2] = a.z; in[3] = a.w;
-                    in[4] = b.x; in[5] = b.y; in[6] = b.z; in[7] = b.w;
-                }
-                const int L = (16 * lu) & 255;  // logical k inside the step
-                const int step = (16 * lu) >> 8;
-                const int gg = L >> 6;
-                uint8_t* rowp = A_s + r * kFRowBytes + step * 512;
-                if constexpr (FMT == IQK_IQ1_S_R4) {
-                    const int mi = (L & 63) >> 3;  // two consecutive 8-weight groups
-                    *(uint4*)(rowp + ((mi * 4 + gg) * 8) * 2) = make_uint4(in[0], in[1], in[2], in[3]);
-                    *(uint4*)(rowp + (((mi + 1) * 4 + gg) * 8) * 2) = make_uint4(in[4], in[5], in[6], in[7]);
-                } else {
-                    const int i = (L & 63) >> 4;  // code word of the chunk
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        uint32_t o[4];
-#pragma unroll
-                        for (int d = 0; d < 4; ++d) {
-                            // (L[4h + d], L[4h + d + 8]) from dwords holding (L[2w], L[2w + 1])
-                            const int x = 4 * h + d;
-                            o[d] = __builtin_amdgcn_perm(in[(x + 8) >> 1], in[x >> 1], (x & 1) ? 0x07060302u : 0x05040100u);
-                        }
-                        *(uint4*)(rowp + (((2 * i + h) * 4 + gg) * 8) * 2) = make_uint4(o[0], o[1], o[2], o[3]);
-                    }
+    for (int e0 = e_first;; e0 += 64) {
+        if (wave == 0) {
+            // row blocks rb of expert e whose cost range starts in [lo, hi)
+            const int e = e0 + lane;
+            int rb0 = 0, rb1 = 0;
+            if (e < p.E) {
+                const int64_t a = p.plan[e];
+                const int64_t cr = rb_cost<N>(p.offsets[e + 1] - p.offsets[e]);
+                if (cr > 0 && a < hi) {
+                    const int64_t s0 = lo > a ? (lo - a + cr - 1) / cr : 0;
+                    const int64_t s1 = (hi - a + cr - 1) / cr;
+                    rb0 = (int)s0;
+                    rb1 = (int)(s1 < nrb ? s1 : nrb);
                 }
             }
-            lds_barrier();
-
-            // k steps of this chunk: raw words one step ahead (the step after
-            // the chunk's last reads nothing)
-            for (int st = 0; st < KC / 256; ++st) {
-                const int c = (kc + 256 * st) / 64 + g;  // this lane's chunk
-                const RowData nxt = load_row<FMT, N>(st + 1 < KC / 256 ? res : none, (uint32_t)row, (uint32_t)(c + 4));
-                u32x4 B[8];
-                decode_chunk<FMT>(cur, c, p.tab, grid_s, B);
-#pragma unroll
-                for (int mi = 0; mi < 8; ++mi) {
-#pragma unroll
-                    for (int m = 0; m < kFMT; ++m) {
-                        if (m < mtc) {
-                            const u32x4 a = *(const u32x4*)(A_s + (m * 16 + li) * kFRowBytes + st * 512 +
-                                                            ((mi * 4 + g) * 8) * 2);
-                            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                             __builtin_bit_cast(bf16x8, B[mi]),
-                                                                             acc[m], 0, 0, 0);
-                        }
-                    }
-                }
-                cur = nxt;
+            cand_rb[lane][0] = rb0;
+            cand_rb[lane][1] = rb1;
+            const uint64_t m = __ballot(rb0 < rb1);
+            if (lane == 0) {
+                cand = m;
+                more = e0 + 64 < p.E && p.plan[e0 + 64] < hi;
             }
         }
-        // D[token 4 g + i][weight row li]
-        if (row < p.out) {
-#pragma unroll
-            for (int m = 0; m < kFMT; ++m) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ti = tb + 16 * m + 4 * g + i;
-                    if (m < mtc && ti < M) p.y[(int64_t)p.perm[base + ti] * p.out + row] = acc[m][i];
-                }
+        __syncthreads();
+        uint64_t m = cand;
+        const int go_on = more;
+        while (m) {
+            const int j = __builtin_ctzll(m);
+            m &= m - 1;
+            const int e = e0 + j;
+            const int rb0 = cand_rb[j][0], rb1 = cand_rb[j][1];
+            const int base = p.offsets[e];
+            const int M = p.offsets[e + 1] - base;
+            const ExpertRes res = expert_res<FMT, N>(p, e);
+            for (int tb = 0; tb < M; tb += 16 * kFMT) {
+                if (M - tb > 16) fused_pass<FMT, N, 2>(p, sh, res, tv, base, M, tb, rb0, rb1, tid, li, g, wave);
+                else fused_pass<FMT, N, 1>(p, sh, res, tv, base, M, tb, rb0, rb1, tid, li, g, wave);
             }
         }
+        if (!go_on) break;
+        __syncthreads();  // every wave has read cand before wave 0 rewrites it
     }
 }
 
+int fused_grid_blocks() {
+    // one block per compute unit (a block's LDS leaves room for no second one)
+    static int cu[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cu[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cu[dev] = n;
+    }
+    return cu[dev];
+}
+
 template <int FMT, int N>
-hipError_t launch_fused_n(const FusedParams& p, hipStream_t s) {
-    const unsigned gx = (unsigned)((p.out + kFRows - 1) / kFRows);
-    hipLaunchKernelGGL((fused_prefill_kernel<FMT, N>), dim3(gx, (unsigned)p.E), dim3(kFThreads), 0, s, p);
+hipError_t launch_fused_n(const FusedParams& p, const int32_t* offsets, int64_t* plan, hipStream_t s) {
+    const int nrb = (p.out + kFRows - 1) / kFRows;
+    hipLaunchKernelGGL((fused_plan_kernel<N>), dim3(1), dim3(kFThreads), 0, s, offsets, p.E, nrb, plan);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((fused_prefill_kernel<FMT, N>), dim3((unsigned)fused_grid_blocks()), dim3(kFThreads), 0, s, p);
     return hipGetLastError();
 }
 
 template <int FMT>
-hipError_t launch_fused_fmt(const FusedParams& p, int64_t n, hipStream_t s) {
-    if (n == 4096) return launch_fused_n<FMT, 4096>(p, s);
-    if (n == 2048) return launch_fused_n<FMT, 2048>(p, s);
-    return launch_fused_n<FMT, 512>(p, s);
+hipError_t launch_fused_fmt(const FusedParams& p, int64_t n, const int32_t* offsets, int64_t* plan, hipStream_t s) {
+    if (n == 4096) return launch_fused_n<FMT, 4096>(p, offsets, plan, s);
+    if (n == 2048) return launch_fused_n<FMT, 2048>(p, offsets, plan, s);
+    return launch_fused_n<FMT, 512>(p, offsets, plan, s);
 }
 
 }  // namespace
@@ -310,9 +598,11 @@ hipError_t launch_fused_prefill(const FusedLaunch& a, hipStream_t s) {
     p.offsets = a.offsets;
     p.perm = a.perm;
     p.y = a.y;
-    if (a.fmt == IQK_IQ2_KS) return launch_fused_fmt<IQK_IQ2_KS>(p, a.n, s);
-    if (a.fmt == IQK_IQ2_K) return launch_fused_fmt<IQK_IQ2_K>(p, a.n, s);
-    return launch_fused_fmt<IQK_IQ1_S_R4>(p, a.n, s);
+    p.y_bytes = a.T * a.k * a.out * 4;
+    p.plan = a.plan;
+    if (a.fmt == IQK_IQ2_KS) return launch_fused_fmt<IQK_IQ2_KS>(p, a.n, a.offsets, a.plan, s);
+    if (a.fmt == IQK_IQ2_K) return launch_fused_fmt<IQK_IQ2_K>(p, a.n, a.offsets, a.plan, s);
+    return launch_fused_fmt<IQK_IQ1_S_R4>(p, a.n, a.offsets, a.plan, s);
 }
 
 }  // namespace iqk

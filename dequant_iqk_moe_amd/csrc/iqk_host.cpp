@@ -534,7 +534,7 @@ int iqk_moe_prefill_fused_workspace(const iqk_weights* w, int64_t T, int k, size
     if (w->experts <= 0 || w->out <= 0 || T < 0 || k <= 0) return fail(IQK_E_ARG, "bad sizes");
     const int64_t P = T * k;
     *bytes = round256((size_t)w->experts * 4) + round256((size_t)(w->experts + 1) * 4) +
-             round256((size_t)std::max<int64_t>(P, 1) * 4);
+             round256((size_t)std::max<int64_t>(P, 1) * 4) + round256((size_t)(w->experts + 1) * 8);
     return ok();
 }
 
@@ -553,6 +553,8 @@ int iqk_moe_prefill_fused(const iqk_weights* w, const float* values, const int8_
     if (w->experts > 16384) return fail(IQK_E_ARG, "prefill routing supports at most 16384 experts");
     if (w->out * (int64_t)iqk::row_bytes(w->fmt, w->in) > 0x7FFFFFFFLL)
         return fail(IQK_E_ARG, "fused prefill needs out * row bytes < 2^31 (out = %lld)", (long long)w->out);
+    if (T * k * w->out * 4 > 0x7FFFFFFFLL)
+        return fail(IQK_E_ARG, "fused prefill needs T * k * out * 4 < 2^31");
     if (w->fmt == IQK_IQ1_S_R4 ? !grid : !values) return fail(IQK_E_ARG, "missing value table or grid");
     size_t need = 0;
     rc = iqk_moe_prefill_fused_workspace(w, T, k, &need);
@@ -567,6 +569,8 @@ int iqk_moe_prefill_fused(const iqk_weights* w, const float* values, const int8_
     int32_t* offsets = (int32_t*)ws;
     ws += round256((size_t)(E + 1) * 4);
     int32_t* perm = (int32_t*)ws;
+    ws += round256((size_t)P * 4);
+    int64_t* plan = (int64_t*)ws;
     hipStream_t s = (hipStream_t)stream;
     iqk::RouteLaunch RL{ids, P, E, sorted, counts, offsets, perm};
     hipError_t e = iqk::launch_route(RL, s);
@@ -583,8 +587,10 @@ int iqk_moe_prefill_fused(const iqk_weights* w, const float* values, const int8_
     FL.x = x_bf16;
     FL.x_slots = x_slots;
     FL.k = k;
+    FL.T = T;
     FL.offsets = offsets;
     FL.perm = perm;
+    FL.plan = plan;
     FL.y = y;
     e = iqk::launch_fused_prefill(FL, s);
     if (e != hipSuccess) return hip_fail(e, "fused prefill launch");

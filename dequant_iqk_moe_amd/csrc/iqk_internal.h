@@ -112,7 +112,9 @@ struct FusedLaunch {
     const int8_t* grid;   // device int8[2048 * 8] (IQ1_S_R4)
     const void* x;        // bf16 [T, x_slots, n]
     int x_slots, k;
+    int64_t T;
     const int32_t *offsets, *perm;
+    int64_t* plan;        // device int64[E + 1] (scratch: per-expert cost prefix)
     float* y;
 };
 

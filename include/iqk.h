@@ -192,8 +192,9 @@ int iqk_grouped_gemm(const void* W_bf16, int64_t E, int64_t out, int64_t in,
                      const void* x_bf16, int x_slots, int64_t T, int k,
                      const int32_t* offsets, const int32_t* perm, float* y, void* stream);
 
-/* Workspace of iqk_moe_prefill_fused: the routing arrays only (counts,
- * offsets, permutation), each rounded up to 256 bytes. */
+/* Workspace of iqk_moe_prefill_fused: the routing arrays (counts, offsets,
+ * permutation) and a work plan of E + 1 int64 (each expert's share of the
+ * kernel's work), each rounded up to 256 bytes. */
 int iqk_moe_prefill_fused_workspace(const iqk_weights* w, int64_t T, int k, size_t* bytes);
 
 /* Prefill with the dequantization fused into the MFMA grouped GEMM (the

@@ -34,6 +34,7 @@ def _weights(fmt, E, out, n, seed):
     (4096, 64, 8, 40, 3, 1),     # two activation chunks of 2048
     (4096, 256, 4, 100, 2, 2),   # ~50 tokens per expert: two passes over k
     (2048, 16, 12, 3, 6, 6),     # most experts idle
+    (512, 768, 160, 80, 4, 1),   # more row blocks than workgroups: runs span several experts
 ])
 def test_fused_prefill_matches_oracle(fmt, n, out, E, T, k, x_slots):
     seed = 1000 + fmt + n // 256 + out + T
@@ -69,3 +70,24 @@ def test_fused_prefill_general_table_invalid_ids_and_two_pass_agreement():
     assert np.all(rel_err_per_vector(y[valid], ref_b[valid]) <= TOL_SAME_WEIGHTS)
     y2 = q.moe_prefill(w, to_dev(x, torch.bfloat16), to_dev(ids), values).cpu().numpy()
     assert np.all(rel_err_per_vector(y[valid], y2[valid].astype(np.float64)) <= TOL_SAME_WEIGHTS)
+
+
+@pytest.mark.parametrize("fmt", [KS, K, R4])
+def test_fused_prefill_skewed_routing(fmt):
+    """One expert takes most pairs (several 32-token tiles), so the work plan
+    spreads its row blocks over many workgroups while idle experts get none."""
+    n, out, E, T, k = 2048, 1024, 8, 160, 2
+    seed = 1200 + fmt
+    announce(f"fused prefill skewed routing fmt={fmt}")
+    w, s = _weights(fmt, E, out, n, seed)
+    values, grid = synth.values_table(seed + 1), synth.ternary_grid(seed + 2)
+    x = bf16_round(synth.normal((T, 1, n), seed + 3))
+    ids = synth.topk_ids(T, k, E, seed + 4)
+    hot = np.arange(T) % 8 != 7          # 140 of 160 tokens send their first pair to expert 0
+    ids[hot, 0] = 0
+    ids[hot, 1] = np.where(ids[hot, 1] == 0, 1, ids[hot, 1])
+    ids[:, 1] = np.where(ids[:, 1] == 5, 3, ids[:, 1])   # expert 5 idle
+    ids[:, 0] = np.where(ids[:, 0] == 5, 4, ids[:, 0])
+    y = q.moe_prefill_fused(w, to_dev(x, torch.bfloat16), to_dev(ids), values, to_dev(grid)).cpu().numpy()
+    ref_b = oracle.moe(fmt, s, E, out, n, x, ids, values, grid, w_bf16=True)
+    assert np.all(rel_err_per_vector(y, ref_b) <= TOL_SAME_WEIGHTS)

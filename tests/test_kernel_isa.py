@@ -1,6 +1,8 @@
 """Checks on the gfx950 assembly of the HIP kernels (CPU only: hipcc
 cross-compiles).  Every kernel must run from registers and LDS alone (no
-scratch: no private segment, no spills), and the deleted-decode floor
+scratch: no private segment, no vector-register spills; scalar registers
+may only be parked in vector-register lanes, which the zero private
+segment guarantees), and the deleted-decode floor
 kernel of each decode matvec instance must issue exactly as many wide code
 loads as the decode kernel itself, so the floor measures the same stream."""
 import os
@@ -50,7 +52,7 @@ def test_no_scratch(src, tmp_path):
     assert meta, "no kernels found"
     for name, m in meta.items():
         assert m.get("private_segment_fixed_size", 0) == 0, name
-        assert m.get("vgpr_spill_count", 0) == 0 and m.get("sgpr_spill_count", 0) == 0, name
+        assert m.get("vgpr_spill_count", 0) == 0, name
 
 
 def test_floor_matvec_issues_the_same_code_loads(tmp_path):
