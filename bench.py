@@ -21,8 +21,10 @@ per second.
 bytes per launch over its average launch duration, from a graph of that
 kernel alone.  `cells` (default on) adds every format x projection x token
 count of the workload family, each with its deleted-decode floor and a plain
-streaming read of the same byte count, plus the prefill rows (routing,
-dequantization producer, MFMA grouped GEMM) at 512 tokens.  `cpu_baseline`
+streaming read of the same byte count, plus the prefill rows at 512 tokens
+(routing, dequantization producer, MFMA grouped GEMM, and the fused prefill
+with the dequantization inside the MFMA GEMM; `--cells prefill` runs only
+these).  `cpu_baseline`
 times the CPU oracle on whole decode steps (about 10 s of CPU work).
 """
 from __future__ import annotations
@@ -50,7 +52,7 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--cells", choices=["none", "all"], default="all")
+    ap.add_argument("--cells", choices=["none", "all", "prefill"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--mode", choices=["bench", "pmc"], default="bench",
@@ -255,6 +257,7 @@ def prefill_cells(ctx, fmt, seed):
     counts, offsets, perm = q.route(ids, E)
     route_ms = timed_eager(torch, lambda i: q.route(ids, E), 50, 5)
     total_ms = route_ms
+    fused_total_ms = 0.0
     out.append({"cell": f"{FMT_NAME[fmt]} prefill route T=512", "kind": "route", "us": round(route_ms * 1e3, 3)})
     grid = ctx.grid if fmt == 3 else None
     for proj, (rows, n) in (("gate_up", (2 * I, H)), ("down", (H, I))):
@@ -287,6 +290,7 @@ def prefill_cells(ctx, fmt, seed):
         dv = dense.view(E * rows, n)
         prod_ms = timed_eager(torch, lambda i: q.dequant(w, ctx.values, grid, torch.bfloat16, out=dv), 10, 2)
         floor_ms = timed_eager(torch, lambda i: q.floor_dequant(w, torch.bfloat16, out=dv), 10, 2)
+        q.dequant(w, ctx.values, grid, torch.bfloat16, out=dv)  # the floor left raw words in the dense copy
         pbytes = wbytes + dbytes
         pg = pbytes / (prod_ms * 1e-3) / 1e9
         out.append({"cell": f"{FMT_NAME[fmt]} prefill producer {proj}", "kind": "producer",
@@ -304,15 +308,36 @@ def prefill_cells(ctx, fmt, seed):
                     "frac_hbm": round(gg / HBM_PEAK_GBS, 4), "TFLOPs": round(tf, 2),
                     "mfma_util": round(tf / BF16_PEAK_TFLOPS, 4), "validation_worst": worst})
         total_ms += prod_ms + gemm_ms
-        del dense, w, y, dv
+        del dense, dv
+        torch.cuda.empty_cache()
+        # the same product with the dequantization inside the MFMA GEMM (route + plan + one kernel)
+        ws = torch.empty(q.prefill_fused_workspace_bytes(w, T, K), dtype=torch.uint8, device="cuda")
+        yf = torch.zeros_like(y)
+        q.moe_prefill_fused(w, x, ids, ctx.values, grid, x_slots=slots, workspace=ws, y=yf)
+        torch.cuda.synchronize()
+        fused_vs_two_pass = float((yf - y).abs().max() / y.abs().max().clamp_min(1e-30))
+        fused_ms = timed_eager(torch, lambda i: q.moe_prefill_fused(w, x, ids, ctx.values, grid, x_slots=slots,
+                                                                      workspace=ws, y=yf), 10, 2)
+        fbytes = wbytes + x.numel() * 2 + y.numel() * 4
+        out.append({"cell": f"{FMT_NAME[fmt]} prefill fused {proj}", "kind": "fused",
+                    "us": round(fused_ms * 1e3, 1), "bytes": int(fbytes),
+                    "GBps": round(fbytes / (fused_ms * 1e-3) / 1e9, 1),
+                    "TFLOPs": round(flops / (fused_ms * 1e-3) / 1e12, 2),
+                    "weights_per_s": round(E * rows * n / (fused_ms * 1e-3), 1),
+                    "max_rel_diff_vs_two_pass": fused_vs_two_pass})
+        fused_total_ms += fused_ms
+        del w, y, yf, ws
         torch.cuda.empty_cache()
     out.append({"cell": f"{FMT_NAME[fmt]} prefill total (route + 2 x (producer + GEMM))", "kind": "prefill",
                 "us": round(total_ms * 1e3, 1), "tokens_per_s": round(T / (total_ms * 1e-3), 1)})
+    out.append({"cell": f"{FMT_NAME[fmt]} prefill total fused (2 x (route + fused GEMM))", "kind": "prefill",
+                "us": round(fused_total_ms * 1e3, 1), "tokens_per_s": round(T / (fused_total_ms * 1e-3), 1)})
     return out
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_iqk2k_gate_up_t1_traffic.md")
-GEMV_SOURCES = ("dequant_iqk_moe_amd/csrc/iqk_gemv.hip", "dequant_iqk_moe_amd/csrc/iqk_internal.h")
+GEMV_SOURCES = ("dequant_iqk_moe_amd/csrc/iqk_gemv.hip", "dequant_iqk_moe_amd/csrc/iqk_device.h",
+                "dequant_iqk_moe_amd/csrc/iqk_internal.h")
 
 
 def measured_traffic():
@@ -457,12 +482,13 @@ def main():
         b1 = 256 * q.row_bytes(q.IQ2_KS, 512) + 512 * 4 + 256 * 4
         cells.append({"cell": "IQ2_KS single [256,512] fp32 x", "kind": "decode", "us": round(ms1 * 1e3, 3),
                       "bytes": b1, "GBps": round(b1 / (ms1 * 1e-3) / 1e9, 2)})
+    if args.cells in ("all", "prefill"):
         ctx.sbuf = None
         torch.cuda.empty_cache()
         for fmt in (q.IQ2_K, q.IQ2_KS, q.IQ1_S_R4):
             cells.extend(prefill_cells(ctx, fmt, 500 + fmt))
-        for c in cells:
-            log(json.dumps(c))
+    for c in cells:
+        log(json.dumps(c))
 
     cpu = None
     if not args.no_cpu_baseline:
