@@ -55,10 +55,11 @@ def _parse():
     ap.add_argument("--cells", choices=["none", "all", "prefill"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=2)
-    ap.add_argument("--mode", choices=["bench", "pmc"], default="bench",
+    ap.add_argument("--mode", choices=["bench", "pmc", "sweep"], default="bench",
                     help="pmc: only launch the headline gate/up matvec 64 times plus two calibration "
                          "kernels of known traffic (a 256 MiB streaming read and a 256 MiB fill), "
-                         "for hardware-counter runs")
+                         "for hardware-counter runs; sweep: decode <-> prefill crossover over "
+                         "T = 1..512 for every format and projection (one JSON line each)")
     return ap.parse_args()
 
 
@@ -384,6 +385,62 @@ def pmc_launches(torch, q, synth, seed):
                       "calibration_bytes": 256 << 20}))
 
 
+def sweep(ctx, fmt, Ts, seed, pools=4):
+    """Decode <-> prefill crossover: for each token count T, the per-pair
+    decode matvec, the fused prefill (route + plan + kernel, dequantization
+    inside the MFMA GEMM) and the two-pass prefill (route + producer + GEMM)
+    on the same weights and routing; one JSON line per (projection, T)."""
+    import synth
+    q, torch = ctx.q, ctx.torch
+    grid = ctx.grid if fmt == 3 else None
+    rows_out = []
+    for proj, (rows, n) in (("gate_up", (2 * I, H)), ("down", (H, I))):
+        slots = 1 if proj == "gate_up" else K
+        pool = Pools(q, torch, fmt, rows, n, seed + (1 if proj == "gate_up" else 2), pools=pools)
+        for T in Ts:
+            S = 8
+            ids_host = [synth.topk_ids(T, K, E, seed * 7919 + T * 31 + i) for i in range(S)]
+            ids = [torch.from_numpy(a).cuda() for a in ids_host]
+            x = torch.from_numpy(synth.normal((T, slots, n), seed + T)).to(torch.bfloat16).cuda()
+            y = torch.zeros((T, K, rows), dtype=torch.float32, device="cuda")
+            yf = torch.zeros_like(y)
+            ws = torch.empty(q.prefill_fused_workspace_bytes(pool.w[0], T, K), dtype=torch.uint8, device="cuda")
+            yg = torch.zeros_like(y)
+            wsg = torch.empty(q.gemv_grouped_workspace_bytes(pool.w[0], T, K), dtype=torch.uint8, device="cuda")
+            q.moe_gemv(pool.w[0], x, ids[0], ctx.values, grid, x_slots=slots, y=y)
+            q.moe_prefill_fused(pool.w[0], x, ids[0], ctx.values, grid, x_slots=slots, workspace=ws, y=yf)
+            q.moe_gemv_grouped(pool.w[0], x, ids[0], ctx.values, grid, x_slots=slots, workspace=wsg, y=yg)
+            torch.cuda.synchronize()
+            diff = float((yf - y).abs().max() / y.abs().max().clamp_min(1e-30))
+            gdiff = float((yg - y).abs().max() / y.abs().max().clamp_min(1e-30))
+            gemv_ms = timed_graph(torch, lambda i: q.moe_gemv(pool.w[i % pools], x, ids[i], ctx.values, grid,
+                                                              x_slots=slots, y=y), S, 4, 1)
+            grouped_ms = timed_eager(torch, lambda i: q.moe_gemv_grouped(pool.w[i % pools], x, ids[i % S], ctx.values,
+                                                                         grid, x_slots=slots, workspace=wsg, y=yg),
+                                     2 * S, pools)
+            fused_ms = timed_eager(torch, lambda i: q.moe_prefill_fused(pool.w[i % pools], x, ids[i % S], ctx.values,
+                                                                        grid, x_slots=slots, workspace=ws, y=yf),
+                                   2 * S, pools)
+            wsz = q.prefill_workspace_bytes(pool.w[0], T, K)
+            ws2 = torch.empty(wsz, dtype=torch.uint8, device="cuda")
+            two_ms = timed_eager(torch, lambda i: q.moe_prefill(pool.w[i % pools], x, ids[i % S], ctx.values, grid,
+                                                                x_slots=slots, workspace=ws2, y=yf), 3, 1)
+            del ws2
+            distinct = float(np.mean([len(np.unique(a)) for a in ids_host]))
+            times = {"gemv": gemv_ms, "grouped_gemv": grouped_ms, "fused_prefill": fused_ms,
+                     "two_pass_prefill": two_ms}
+            row = {"sweep": FMT_NAME[fmt], "proj": proj, "T": T, "pairs": T * K, "distinct_experts": distinct,
+                   **{k + "_us": round(v * 1e3, 1) for k, v in times.items()},
+                   "best": min(times, key=times.get), "fused_vs_gemv_max_rel_diff": diff,
+                   "grouped_vs_gemv_max_rel_diff": gdiff}
+            log(json.dumps(row))
+            rows_out.append(row)
+            del y, yf, yg, ws, wsg, x
+        del pool
+        torch.cuda.empty_cache()
+    return rows_out
+
+
 def main():
     args = _parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -400,6 +457,16 @@ def main():
     torch.cuda.set_device(0)
     if args.mode == "pmc":
         pmc_launches(torch, q, synth, args.seed)
+        return
+    if args.mode == "sweep":
+        ctx = Ctx(q, torch, args.seed)
+        rows = []
+        for fmt in (q.IQ2_K, q.IQ2_KS, q.IQ1_S_R4):
+            rows += sweep(ctx, fmt, (1, 2, 4, 8, 16, 32, 64, 128, 256, 512), 900 + fmt)
+        best = {}
+        for r in rows:
+            best.setdefault(f"{r['sweep']} {r['proj']}", []).append((r["T"], r["best"]))
+        print(json.dumps({"sweep_rows": len(rows), "best_path_by_T": best}), flush=True)
         return
     T = 1
     # steps per captured graph: the largest divisor of K up to 64, so exactly K steps are timed

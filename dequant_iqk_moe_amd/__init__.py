@@ -81,6 +81,8 @@ def _load():
         "iqk_moe_gemv": (i32, [W, p, p, p, i32, i32, p, i64, i32, p, p]),
         "iqk_moe_gemv_swiglu": (i32, [W, p, p, p, i32, i32, p, i64, i32, p, p]),
         "iqk_moe_gemv_combine": (i32, [W, p, p, p, i32, i32, p, p, i64, i32, p, p]),
+        "iqk_moe_gemv_grouped_workspace": (i32, [W, i64, i32, p]),
+        "iqk_moe_gemv_grouped": (i32, [W, p, p, p, i32, i32, p, i64, i32, i32, p, sz, p, p]),
         "iqk_route": (i32, [p, i64, i64, i32, p, p, p, p]),
         "iqk_grouped_gemm": (i32, [p, i64, i64, i64, p, i32, i64, i32, p, p, p, p]),
         "iqk_moe_prefill_workspace": (i32, [W, i64, i32, p]),
@@ -259,6 +261,34 @@ def moe_gemv_combine(w: Weights, x: torch.Tensor, ids: torch.Tensor, route_w: to
     cw = w._c()
     _check(_lib.iqk_moe_gemv_combine(ctypes.byref(cw), vp, _dev(grid, "grid", torch.int8), xp, xdt, x_slots,
                                      _dev(ids, "ids", torch.int32), _dev(route_w, "route_w", torch.float32), T, k,
+                                     _dev(y, "y", torch.float32), _stream(stream)))
+    return y
+
+
+def gemv_grouped_workspace_bytes(w: Weights, T: int, k: int) -> int:
+    b = ctypes.c_size_t()
+    cw = _Weights(_fmt(w.fmt), w.experts, w.out, w.in_features, None, 0)
+    _check(_lib.iqk_moe_gemv_grouped_workspace(ctypes.byref(cw), T, k, ctypes.byref(b)))
+    return b.value
+
+
+def moe_gemv_grouped(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=None, grid: torch.Tensor | None = None,
+                     x_slots: int = 1, sorted: bool = False, workspace: torch.Tensor | None = None,
+                     y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Grouped decode matvec: route, then one decode pass per selected expert
+    shared by all of its pairs.  y[T, k, out] (float32); pairs with an
+    invalid id leave their rows untouched."""
+    T, k = ids.shape
+    xp, xdt = _x_args(x, T, x_slots, w.in_features)
+    if workspace is None:
+        workspace = torch.empty(gemv_grouped_workspace_bytes(w, T, k), dtype=torch.uint8, device=w.streams.device)
+    if y is None:
+        y = torch.zeros((T, k, w.out), dtype=torch.float32, device=w.streams.device)
+    _v, vp = _host_values(values)
+    cw = w._c()
+    _check(_lib.iqk_moe_gemv_grouped(ctypes.byref(cw), vp, _dev(grid, "grid", torch.int8), xp, xdt, x_slots,
+                                     _dev(ids, "ids", torch.int32), T, k, int(bool(sorted)),
+                                     _dev(workspace, "workspace", torch.uint8), workspace.numel(),
                                      _dev(y, "y", torch.float32), _stream(stream)))
     return y
 

@@ -757,6 +757,424 @@ hipError_t launch_fmt(const GemvParams& p, int fmt, int64_t n, int xdt, int64_t 
     return launch_n<IQK_IQ1_S_R4, FLOOR, MODE>(p, n, xdt, T, s);
 }
 
+// ---------------------------------------------------------------------------
+// Grouped decode matvec: the pairs routed to one expert in one pass over its
+// rows.  Each 64-weight chunk is decoded once into int8 weight words and
+// then multiplied with every token of the pass, so the decode (and the HBM
+// read) is shared by the expert's tokens.  A lane's chunk of k is the same
+// for every row it visits, so the pass's activations live in its registers
+// (converted by the lane itself) and the inner loop touches no LDS.
+// ---------------------------------------------------------------------------
+
+constexpr int kGWaves = 8;  // waves per workgroup (256 registers per lane)
+// tokens per pass over an expert's rows: their activations stay in
+// registers (a float32 activation needs more registers to convert)
+template <int XDT>
+constexpr int grouped_tok() { return XDT == IQK_BF16 ? 4 : 3; }
+
+struct GroupedParams {
+    const uint8_t* S;
+    int64_t off0, off1, off2, off3, off4;
+    int32_t E, out;
+    uint32_t tab_lo, tab_hi;
+    float tab_scale;
+    const int8_t* grid;
+    const void* x;
+    int32_t x_slots, k;
+    const int32_t* offsets;  // [E + 1] from the routing gather
+    const int32_t* perm;     // expert-sorted pair indices
+    const int64_t* plan;     // [E + 1] cost prefix
+    float* y;                // [T * k, out]
+    int64_t y_bytes;
+    int32_t upo;             // reduction groups per expert
+};
+
+// One lane's 64 activations of one token, in the fixed point of the per-pair
+// matvec (the same scale, bytes and word order as its LDS copy).
+struct XLane {
+    uint32_t hi[16], lo[16];
+    float scale;       // 2^(emax - 13) times the table scale
+    int32_t bsum[2];   // IQ1_S_R4: sums of the fixed-point values per 32
+};
+
+template <int XDT>
+__device__ __forceinline__ void lane_block(const void* xrow, int c, int blk, float* v) {
+    if constexpr (XDT == IQK_BF16) {
+        const uint4* src = (const uint4*)xrow + 8 * c + 2 * blk;
+        const uint4 a = src[0], b = src[1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    } else {
+        const uint4* src = (const uint4*)xrow + 16 * c + 4 * blk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 a = src[i];
+            v[4 * i] = __uint_as_float(a.x);
+            v[4 * i + 1] = __uint_as_float(a.y);
+            v[4 * i + 2] = __uint_as_float(a.z);
+            v[4 * i + 3] = __uint_as_float(a.w);
+        }
+    }
+}
+
+// (two passes over the 64 values, 16 at a time: the maximum, then the
+// conversion; the second pass reads them again from the cache)
+template <int FMT, int XDT>
+__device__ __forceinline__ void lane_x(const void* xrow, int c, float tab_scale, XLane& o) {
+    uint32_t amax = 0;
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+        float v[16];
+        lane_block<XDT>(xrow, c, blk, v);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = max(amax, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+    }
+    int emax = (int)(amax >> 23) - 127;
+    emax = emax < -100 ? -100 : emax;
+    const float sc = __builtin_ldexpf(1.0f, 13 - emax);
+    int32_t bs[2] = {0, 0};
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+        float v[16];
+        lane_block<XDT>(xrow, c, blk, v);
+        int hi[16], lo[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int q = (int)__builtin_rintf(v[i] * sc);  // |q| <= 2^14
+            hi[i] = (q + 128) >> 8;
+            lo[i] = q - (hi[i] << 8);
+            bs[blk >> 1] += q;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i0 = FMT == IQK_IQ1_S_R4 ? 4 * j : j;
+            const int st = FMT == IQK_IQ1_S_R4 ? 1 : 4;
+            o.hi[4 * blk + j] = (uint32_t)(hi[i0] & 0xFF) | ((uint32_t)(hi[i0 + st] & 0xFF) << 8) |
+                                ((uint32_t)(hi[i0 + 2 * st] & 0xFF) << 16) | ((uint32_t)(hi[i0 + 3 * st] & 0xFF) << 24);
+            o.lo[4 * blk + j] = (uint32_t)(lo[i0] & 0xFF) | ((uint32_t)(lo[i0 + st] & 0xFF) << 8) |
+                                ((uint32_t)(lo[i0 + 2 * st] & 0xFF) << 16) | ((uint32_t)(lo[i0 + 3 * st] & 0xFF) << 24);
+        }
+    }
+    o.scale = __builtin_ldexpf(1.0f, emax - 13) * tab_scale;
+    o.bsum[0] = bs[0];
+    o.bsum[1] = bs[1];
+}
+
+// One lane's decoded 64-weight chunk of one row: int8 weight words w[i]
+// (word i pairs with activation word i of the chunk), the sub-block scale
+// indices (2-bit members), the block scales and shifts (IQ1_S_R4), the row
+// scale.
+struct Dec {
+    uint32_t w[16];
+    int si[4];
+    float fs[2], fh[2];
+    float d;
+};
+
+template <int FMT>
+__device__ __forceinline__ void decode_chunk(Dec& o, const RowData& r, int c, uint32_t tlo, uint32_t thi,
+                                             const uint2* grid_s) {
+    o.d = half_to_float(r.d);
+    if constexpr (FMT == IQK_IQ2_K) {
+        const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+        const uint32_t sc = r.a ^ 0x8888u;
+        const uint32_t sx = r.b >> (4 * (c & 1));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)sx, i, 1) & 0x04040404u;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                o.w[4 * i + jj] = __builtin_amdgcn_perm(thi, tlo, and_or_fast(q[i] >> (2 * jj), 0x03030303u, m));
+            o.si[i] = __builtin_amdgcn_sbfe((int)sc, 4 * i, 4);
+        }
+    } else if constexpr (FMT == IQK_IQ2_KS) {
+        const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+        const int sh = 2 * (c & 3);
+        const uint32_t schx = ~r.b;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const uint32_t raw = ((r.a >> (4 * s)) & 15u) | (((schx >> (sh + s)) & 1u) << 4);
+            o.si[s] = __builtin_amdgcn_sbfe((int)raw, 0, 5);
+            const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)r.c, sh + s, 1) & 0x04040404u;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    o.w[4 * (2 * s + t) + jj] =
+                        __builtin_amdgcn_perm(thi, tlo, and_or_fast(q[2 * s + t] >> (2 * jj), 0x03030303u, m));
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const uint32_t h16 = (r.a >> (16 * b)) & 0xFFFFu;
+            const uint32_t qsw = b == 0 ? r.q.x : r.q.y;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int g = 4 * b + j;
+                const uint32_t idx = ((qsw >> (8 * j)) & 0xFFu) | (((h16 >> (3 * j)) & 7u) << 8);
+                const uint2 gv = grid_s[idx];
+                o.w[2 * g] = gv.x;
+                o.w[2 * g + 1] = gv.y;
+            }
+            o.fh[b] = (h16 >> 15) ? -0.125f : 0.125f;
+            o.fs[b] = (float)(2 * ((h16 >> 12) & 7u) + 1);
+        }
+    }
+}
+
+// The decoded chunk against one token's activations, before the per-lane
+// float scale: the same integer sums and float steps as the per-pair matvec.
+template <int FMT>
+__device__ __forceinline__ float dot_chunk(const Dec& o, const XLane& x) {
+    int h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h[i] = dot4_first(o.w[4 * i], x.hi[4 * i]);
+        l[i] = dot4_first(o.w[4 * i], x.lo[4 * i]);
+#pragma unroll
+        for (int jj = 1; jj < 4; ++jj) {
+            h[i] = __builtin_amdgcn_sdot4((int)o.w[4 * i + jj], (int)x.hi[4 * i + jj], h[i], false);
+            l[i] = __builtin_amdgcn_sdot4((int)o.w[4 * i + jj], (int)x.lo[4 * i + jj], l[i], false);
+        }
+    }
+    if constexpr (FMT == IQK_IQ2_K) {
+        int ah = 0, al = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ah += __mul24(h[i], o.si[i]);
+            al += __mul24(l[i], o.si[i]);
+        }
+        return (float)ah * 256.0f + (float)al;
+    } else if constexpr (FMT == IQK_IQ2_KS) {
+        int ah = 0, al = 0;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            ah += __mul24(h[2 * s] + h[2 * s + 1], o.si[s]);
+            al += __mul24(l[2 * s] + l[2 * s + 1], o.si[s]);
+        }
+        return (float)ah * 256.0f + (float)al;
+    } else {
+        float part = 0.f;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int ah = h[2 * b] + h[2 * b + 1], al = l[2 * b] + l[2 * b + 1];
+            const float tb = (float)ah * 256.0f + (float)al + o.fh[b] * (float)x.bsum[b];
+            part += tb * o.fs[b];
+        }
+        return part;
+    }
+}
+
+// Cost of one reduction group of an expert with M tokens: a decode per pass
+// of up to MT tokens plus one multiply per token (decode about 5/3 of a
+// token's multiply in instructions).
+template <int MT>
+__device__ __forceinline__ int64_t grouped_unit_cost(int M) {
+    return (int64_t)5 * ((M + MT - 1) / MT) + 3 * (int64_t)M;
+}
+
+// plan[e] = cost of all reduction groups of experts before e (one workgroup).
+template <int MT>
+__global__ __launch_bounds__(1024) void grouped_plan_kernel(const int32_t* offsets, int E, int upo, int64_t* plan) {
+    __shared__ int64_t part[1024];
+    const int tid = threadIdx.x;
+    int64_t carry = 0;
+    if (tid == 0) plan[0] = 0;
+    for (int c0 = 0; c0 < E; c0 += 1024) {
+        const int e = c0 + tid;
+        part[tid] = e < E ? grouped_unit_cost<MT>(offsets[e + 1] - offsets[e]) * upo : 0;
+        __syncthreads();
+        for (int o = 1; o < 1024; o <<= 1) {
+            const int64_t add = tid >= o ? part[tid - o] : 0;
+            __syncthreads();
+            part[tid] += add;
+            __syncthreads();
+        }
+        if (e < E) plan[e + 1] = carry + part[tid];
+        carry += part[1023];
+        __syncthreads();
+    }
+}
+
+// Workgroup b of G takes the reduction groups whose cost range starts in
+// [b C / G, (b + 1) C / G), C = plan[E]: a contiguous run over the
+// expert-sorted list, so a workgroup converts each expert's activations
+// once per pass and spans few experts.
+template <int FMT, int N, int XDT>
+__global__ __launch_bounds__(64 * kGWaves) void gemv_grouped_kernel(GroupedParams p) {
+    using G = Geo<N>;
+    constexpr int kGTok = grouped_tok<XDT>();
+    __shared__ uint2 grid_s[FMT == IQK_IQ1_S_R4 ? 2048 : 1];
+    __shared__ int32_t e_first;
+    __shared__ uint64_t cand;  // experts e0 .. e0 + 63 with groups in this block
+    __shared__ int32_t cand_g[64][2];
+    __shared__ int32_t more;
+
+    const int nthreads = blockDim.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nwaves = nthreads >> 6;
+    const int64_t C = p.plan[p.E];
+    const int64_t lo = C * blockIdx.x / gridDim.x, hi = C * (blockIdx.x + 1) / gridDim.x;
+    if (lo >= hi) return;
+
+    if constexpr (FMT == IQK_IQ1_S_R4) {
+        for (int i = tid; i < 1024; i += nthreads) ((uint4*)grid_s)[i] = ((const uint4*)p.grid)[i];
+    }
+    for (int e = tid; e < p.E; e += nthreads)
+        if (p.plan[e] <= lo && p.plan[e + 1] > lo) e_first = e;
+    __syncthreads();
+
+    const int c = lane % G::LPR;  // chunk of k owned by this lane
+    const int lane_row = lane / G::LPR;
+    const Rsrc yres = make_rsrc(p.y, (uint32_t)p.y_bytes);
+    auto xrow_ptr = [&](int xr) {
+        const int64_t xoff = (int64_t)xr * N;
+        return XDT == IQK_BF16 ? (const void*)((const uint16_t*)p.x + xoff) : (const void*)((const float*)p.x + xoff);
+    };
+
+    for (int e0 = e_first;; e0 += 64) {
+        if (wave == 0) {
+            const int e = e0 + lane;
+            int g0 = 0, g1 = 0;
+            if (e < p.E) {
+                const int64_t a = p.plan[e];
+                const int64_t cr = grouped_unit_cost<kGTok>(p.offsets[e + 1] - p.offsets[e]);
+                if (p.offsets[e + 1] > p.offsets[e] && a < hi) {
+                    const int64_t s0 = lo > a ? (lo - a + cr - 1) / cr : 0;
+                    const int64_t s1 = (hi - a + cr - 1) / cr;
+                    g0 = (int)s0;
+                    g1 = (int)(s1 < p.upo ? s1 : p.upo);
+                }
+            }
+            cand_g[lane][0] = g0;
+            cand_g[lane][1] = g1;
+            const uint64_t m = __ballot(g0 < g1);
+            if (lane == 0) {
+                cand = m;
+                more = e0 + 64 < p.E && p.plan[e0 + 64] < hi;
+            }
+        }
+        __syncthreads();
+        uint64_t cm = cand;
+        const int go_on = more;
+        while (cm) {
+            const int j = __builtin_ctzll(cm);
+            cm &= cm - 1;
+            const int e = e0 + j;
+            const int g0 = cand_g[j][0], g1 = cand_g[j][1];
+            const int base = p.offsets[e];
+            const int M = p.offsets[e + 1] - base;
+            const ExpertRes res = expert_res<FMT, N>(p, e);
+            const int ng = g1 - g0;
+            const int my = wave < ng ? (ng - wave + nwaves - 1) / nwaves : 0;
+            if (my == 0) continue;
+            for (int ps = 0; ps < M; ps += kGTok) {
+                const int mp = min(kGTok, M - ps);
+                // rows of a group past `out` (and of a finished wave) read row
+                // `out`, an out-of-range offset: zeros, never stored
+                auto row_of = [&](int g, int it) { return g * G::RPG + it * G::RPI + lane_row; };
+                Group<FMT, N> raw;
+#pragma unroll
+                for (int it = 0; it < G::GIT; ++it) {
+                    const int r = row_of(g0 + wave, it);
+                    raw.r[it] = load_row<FMT, N>(res, (uint32_t)(r < p.out ? r : p.out), (uint32_t)c);
+                }
+                // the pass's activations, this lane's chunk of each
+                XLane xs[kGTok];
+                int pr[kGTok];
+#pragma unroll
+                for (int mm = 0; mm < kGTok; ++mm) {
+                    pr[mm] = 0;
+                    if (mm < mp) {
+                        const int pair = p.perm[base + ps + mm];
+                        pr[mm] = pair;
+                        lane_x<FMT, XDT>(xrow_ptr(p.x_slots == 1 ? pair / p.k : pair), c, p.tab_scale, xs[mm]);
+                    }
+                }
+                for (int item = 0; item < my; ++item) {
+                    const int g = g0 + wave + item * nwaves;
+                    const int gn = g + nwaves;
+                    const bool nlive = item + 1 < my;
+                    float part[kGTok][G::GIT];
+#pragma unroll
+                    for (int it = 0; it < G::GIT; ++it) {
+                        Dec dec;
+                        decode_chunk<FMT>(dec, raw.r[it], c, p.tab_lo, p.tab_hi, grid_s);
+                        // this row's slot now loads the same row of the next group
+                        const int rn = row_of(gn, it);
+                        raw.r[it] = load_row<FMT, N>(res, (uint32_t)(nlive && rn < p.out ? rn : p.out), (uint32_t)c);
+#pragma unroll
+                        for (int mm = 0; mm < kGTok; ++mm)
+                            if (mm < mp) part[mm][it] = dot_chunk<FMT>(dec, xs[mm]) * (dec.d * xs[mm].scale);
+                    }
+#pragma unroll
+                    for (int mm = 0; mm < kGTok; ++mm) {
+                        if (mm < mp) {
+                            uint32_t pu[G::GIT];
+#pragma unroll
+                            for (int it = 0; it < G::GIT; ++it) pu[it] = __float_as_uint(part[mm][it]);
+                            int q;
+                            bool writer;
+                            const uint32_t sum = reduce_group<N, false>(pu, lane, &q, &writer);
+                            const int row = g * G::RPG + q;
+                            const uint32_t off = (uint32_t)(pr[mm] * p.out + row) * 4u;
+                            __builtin_amdgcn_raw_buffer_store_b32(sum, yres, writer && row < p.out ? off : kOob, 0, 0);
+                        }
+                    }
+                }
+            }
+        }
+        if (!go_on) break;
+        __syncthreads();  // every wave has read cand before wave 0 rewrites it
+    }
+}
+
+int grouped_grid_blocks() {
+    // one large workgroup per compute unit
+    static int cu[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cu[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cu[dev] = n;
+    }
+    return cu[dev];
+}
+
+template <int FMT, int N, int XDT>
+hipError_t launch_grouped_inst(GroupedParams p, hipStream_t s) {
+    using G = Geo<N>;
+    p.upo = (int32_t)((p.out + G::RPG - 1) / G::RPG);
+    int64_t* plan = const_cast<int64_t*>(p.plan);
+    hipLaunchKernelGGL((grouped_plan_kernel<grouped_tok<XDT>()>), dim3(1), dim3(1024), 0, s, p.offsets, (int)p.E,
+                       (int)p.upo, plan);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemv_grouped_kernel<FMT, N, XDT>), dim3((unsigned)grouped_grid_blocks()), dim3(64 * kGWaves),
+                       0, s, p);
+    return hipGetLastError();
+}
+
+template <int FMT, int N>
+hipError_t launch_grouped_x(const GroupedParams& p, int xdt, hipStream_t s) {
+    if (xdt == IQK_BF16) return launch_grouped_inst<FMT, N, IQK_BF16>(p, s);
+    return launch_grouped_inst<FMT, N, IQK_F32>(p, s);
+}
+
+template <int FMT>
+hipError_t launch_grouped_n(const GroupedParams& p, int64_t n, int xdt, hipStream_t s) {
+    if (n == 4096) return launch_grouped_x<FMT, 4096>(p, xdt, s);
+    if (n == 2048) return launch_grouped_x<FMT, 2048>(p, xdt, s);
+    return launch_grouped_x<FMT, 512>(p, xdt, s);
+}
+
 }  // namespace
 
 hipError_t launch_gemv(const GemvLaunch& a, bool floor_variant, hipStream_t s) {
@@ -786,6 +1204,39 @@ hipError_t launch_gemv(const GemvLaunch& a, bool floor_variant, hipStream_t s) {
     if (a.mode == kSwiGLU) return launch_fmt<false, kSwiGLU>(p, a.fmt, a.n, a.x_dtype, a.T, s);
     if (a.mode == kCombine) return launch_fmt<false, kCombine>(p, a.fmt, a.n, a.x_dtype, a.T, s);
     return launch_fmt<false, kPlain>(p, a.fmt, a.n, a.x_dtype, a.T, s);
+}
+
+}  // namespace iqk
+
+namespace iqk {
+
+hipError_t launch_gemv_grouped(const GemvLaunch& a, const int32_t* offsets, const int32_t* perm, int64_t* plan,
+                               hipStream_t s) {
+    GroupedParams p;
+    p.S = a.streams;
+    p.off0 = a.pl.off[0];
+    p.off1 = a.pl.off[1];
+    p.off2 = a.pl.off[2];
+    p.off3 = a.pl.off[3];
+    p.off4 = a.pl.off[4];
+    p.E = (int32_t)a.E;
+    p.out = (int32_t)a.out;
+    p.tab_lo = a.tab_lo;
+    p.tab_hi = a.tab_hi;
+    p.tab_scale = a.tab_scale;
+    p.grid = a.grid;
+    p.x = a.x;
+    p.x_slots = a.x_slots;
+    p.k = a.k;
+    p.offsets = offsets;
+    p.perm = perm;
+    p.plan = plan;
+    p.y = a.y;
+    p.y_bytes = a.T * a.k * a.out * 4;
+    p.upo = 0;
+    if (a.fmt == IQK_IQ2_KS) return launch_grouped_n<IQK_IQ2_KS>(p, a.n, a.x_dtype, s);
+    if (a.fmt == IQK_IQ2_K) return launch_grouped_n<IQK_IQ2_K>(p, a.n, a.x_dtype, s);
+    return launch_grouped_n<IQK_IQ1_S_R4>(p, a.n, a.x_dtype, s);
 }
 
 }  // namespace iqk

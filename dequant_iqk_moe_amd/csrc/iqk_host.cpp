@@ -597,6 +597,50 @@ int iqk_moe_prefill_fused(const iqk_weights* w, const float* values, const int8_
     return ok();
 }
 
+int iqk_moe_gemv_grouped_workspace(const iqk_weights* w, int64_t T, int k, size_t* bytes) {
+    if (!w || !bytes) return fail(IQK_E_ARG, "null pointer");
+    int rc = check_fmt_shape(w->fmt, w->in);
+    if (rc) return rc;
+    if (w->experts <= 0 || w->out <= 0 || T < 0 || k <= 0) return fail(IQK_E_ARG, "bad sizes");
+    const int64_t P = T * k;
+    *bytes = round256((size_t)w->experts * 4) + round256((size_t)(w->experts + 1) * 4) +
+             round256((size_t)std::max<int64_t>(P, 1) * 4) + round256((size_t)(w->experts + 1) * 8);
+    return ok();
+}
+
+int iqk_moe_gemv_grouped(const iqk_weights* w, const float* values, const int8_t* grid, const void* x, int x_dtype,
+                         int x_slots, const int32_t* ids, int64_t T, int k, int sorted, void* workspace,
+                         size_t ws_bytes, float* y, void* stream) {
+    iqk::GemvLaunch L;
+    int rc = check_gemv_args(w, values, grid, x, x_dtype, x_slots, ids, T, k, y, &L);
+    if (rc) return rc;
+    if (sorted != 0 && sorted != 1) return fail(IQK_E_ARG, "sorted must be 0 or 1");
+    if (w->experts > 16384) return fail(IQK_E_ARG, "routing supports at most 16384 experts");
+    if (T * k * w->out * 4 > 0x7FFFFFFFLL) return fail(IQK_E_ARG, "grouped matvec needs T * k * out * 4 < 2^31");
+    size_t need = 0;
+    rc = iqk_moe_gemv_grouped_workspace(w, T, k, &need);
+    if (rc) return rc;
+    if (!workspace || ws_bytes < need) return fail(IQK_E_SIZE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+    if (T == 0) return ok();
+    L.y = y;
+    const int64_t E = w->experts, P = T * k;
+    uint8_t* ws = (uint8_t*)workspace;
+    int32_t* counts = (int32_t*)ws;
+    ws += round256((size_t)E * 4);
+    int32_t* offsets = (int32_t*)ws;
+    ws += round256((size_t)(E + 1) * 4);
+    int32_t* perm = (int32_t*)ws;
+    ws += round256((size_t)P * 4);
+    int64_t* plan = (int64_t*)ws;
+    hipStream_t s = (hipStream_t)stream;
+    iqk::RouteLaunch RL{ids, P, E, sorted, counts, offsets, perm};
+    hipError_t e = iqk::launch_route(RL, s);
+    if (e != hipSuccess) return hip_fail(e, "grouped matvec route launch");
+    e = iqk::launch_gemv_grouped(L, offsets, perm, plan, s);
+    if (e != hipSuccess) return hip_fail(e, "grouped matvec launch");
+    return ok();
+}
+
 int iqk_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, void* stream) {
     if (!buf || !sink || bytes == 0 || bytes % 16 || sink_words == 0) return fail(IQK_E_ARG, "bad stream-read arguments");
     hipError_t e = iqk::launch_stream_read(buf, bytes, sink, sink_words, (hipStream_t)stream);

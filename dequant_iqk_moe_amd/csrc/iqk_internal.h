@@ -121,6 +121,10 @@ struct FusedLaunch {
 hipError_t launch_dequant(const DequantLaunch& a, bool floor_variant, hipStream_t s);
 hipError_t launch_fused_prefill(const FusedLaunch& a, hipStream_t s);
 hipError_t launch_gemv(const GemvLaunch& a, bool floor_variant, hipStream_t s);
+// grouped decode matvec (plain y): routing arrays from launch_route, plan =
+// device int64[E + 1] scratch
+hipError_t launch_gemv_grouped(const GemvLaunch& a, const int32_t* offsets, const int32_t* perm, int64_t* plan,
+                               hipStream_t s);
 hipError_t launch_route(const RouteLaunch& a, hipStream_t s);
 hipError_t launch_grouped_gemm(const GemmLaunch& a, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, hipStream_t s);

@@ -32,6 +32,7 @@ namespace {
 
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteMaxE = 16384;
+constexpr int kRouteStage = 4096;  // ids staged in LDS per scatter chunk
 
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids, int32_t P, int32_t E,
                                                               int32_t* __restrict__ counts,
@@ -39,6 +40,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
                                                               int32_t* __restrict__ perm) {
     __shared__ int32_t cur[kRouteMaxE];
     __shared__ int32_t part[kRouteThreads];
+    __shared__ int32_t stage[kRouteStage];
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += kRouteThreads) cur[e] = 0;
     __syncthreads();
@@ -70,33 +72,40 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
     }
     if (tid == kRouteThreads - 1) offsets[E] = part[tid];
     const int total = part[kRouteThreads - 1];
-    __syncthreads();
-    if (tid < 64) {
-        // stable scatter, one wave, 64 pairs per step
-        const uint64_t lt = (1ull << tid) - 1ull;
-        int nbits = 1;
-        while ((1 << nbits) < E) ++nbits;
-        for (int base = 0; base < P; base += 64) {
-            const int p = base + tid;
-            const int e = p < P ? ids[p] : -1;
-            const bool valid = e >= 0 && e < E;
-            uint64_t same = __ballot(valid);
-            for (int b = 0; b < nbits; ++b) {
-                const bool bit = valid && ((e >> b) & 1);
-                const uint64_t m = __ballot(bit);
-                same &= bit ? m : ~m;
+    // positions past the valid pairs (invalid ids are dropped)
+    for (int p = total + tid; p < P; p += kRouteThreads) perm[p] = -1;
+    // stable scatter: the ids are staged in LDS a chunk at a time by the
+    // whole workgroup, then one wave ranks 64 pairs per step (equal ids
+    // found with one ballot per id bit) and advances the cursors
+    int nbits = 1;
+    while ((1 << nbits) < E) ++nbits;
+    const uint64_t lt = (1ull << (tid & 63)) - 1ull;
+    for (int base = 0; base < P; base += kRouteStage) {
+        const int n = min(kRouteStage, P - base);
+        __syncthreads();  // the cursors are final / the previous chunk is ranked
+        for (int i = tid; i < n; i += kRouteThreads) stage[i] = ids[base + i];
+        __syncthreads();
+        if (tid < 64) {
+            for (int s0 = 0; s0 < n; s0 += 64) {
+                const int i = s0 + tid;
+                const int e = i < n ? stage[i] : -1;
+                const bool valid = e >= 0 && e < E;
+                uint64_t same = __ballot(valid);
+                for (int b = 0; b < nbits; ++b) {
+                    const bool bit = valid && ((e >> b) & 1);
+                    const uint64_t m = __ballot(bit);
+                    same &= bit ? m : ~m;
+                }
+                const int rank = __popcll(same & lt);
+                const int cnt = __popcll(same);
+                int pos = 0;
+                if (valid) pos = cur[e] + rank;
+                __builtin_amdgcn_wave_barrier();
+                if (valid && rank == cnt - 1) cur[e] = pos + 1;  // last of its expert advances the cursor
+                __builtin_amdgcn_wave_barrier();
+                if (valid) perm[pos] = base + i;
             }
-            const int rank = __popcll(same & lt);
-            const int cnt = __popcll(same);
-            int pos = 0;
-            if (valid) pos = cur[e] + rank;
-            __builtin_amdgcn_wave_barrier();
-            if (valid && rank == cnt - 1) cur[e] = pos + 1;  // last of its expert advances the cursor
-            __builtin_amdgcn_wave_barrier();
-            if (valid) perm[pos] = p;
         }
-    } else {
-        for (int p = total + tid - 64; p < P; p += kRouteThreads - 64) perm[p] = -1;
     }
 }
 

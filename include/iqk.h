@@ -170,6 +170,29 @@ int iqk_moe_gemv_combine(const iqk_weights* w, const float* values, const int8_t
                          const void* x, int x_dtype, int x_slots, const int32_t* ids,
                          const float* route_w, int64_t T, int k, float* y, void* stream);
 
+/* Workspace of iqk_moe_gemv_grouped: the routing arrays (counts, offsets,
+ * permutation) and a work plan of E + 1 int64, each rounded up to 256
+ * bytes. */
+int iqk_moe_gemv_grouped_workspace(const iqk_weights* w, int64_t T, int k, size_t* bytes);
+
+/* Grouped decode matvec for a few tokens per expert (between the per-pair
+ * matvec and the prefill in "Surface"'s dispatch by the number of
+ * token-expert pairs): iqk_route, then one pass over each selected expert's
+ * rows that decodes every 64-weight chunk once and multiplies it with all of
+ * the expert's pairs (4 per pass for a bf16 activation, 3 for float32; the
+ * pass's activations are held in registers), so an expert chosen by several
+ * tokens is read and decoded once per pass.  Arguments, value-table rule, accuracy
+ * and widths as iqk_moe_gemv; workspace from iqk_moe_gemv_grouped_workspace;
+ * `sorted` as iqk_route.  Per pair the sums are formed as in iqk_moe_gemv
+ * (the two agree to float32 rounding).  Pairs with an invalid id leave
+ * their rows of y untouched (they are dropped by the routing, as in the
+ * prefill calls).  Limits: as iqk_moe_gemv, E <= 16384, T * k * out * 4 <
+ * 2^31. */
+int iqk_moe_gemv_grouped(const iqk_weights* w, const float* values, const int8_t* grid,
+                         const void* x, int x_dtype, int x_slots, const int32_t* ids,
+                         int64_t T, int k, int sorted, void* workspace, size_t ws_bytes,
+                         float* y, void* stream);
+
 /* Routing gather ("Surface": sorting pairs by expert so that each expert's
  * weights are read once).  ids: device int32 [P] (P = T*k pair indices
  * t*k + j).  Writes device int32 counts[E], offsets[E+1] (exclusive prefix

@@ -136,6 +136,23 @@ def test_validation_errors_before_any_launch():
     assert nb.value == 4 * 64 * 512 * 2 + 256 + 256 + 256
     assert L.iqk_moe_prefill(ctypes.byref(w), vp, None, fake, 1, fake, 8, 6, 0, fake, nb.value - 1, fake, s0) == q._E_SIZE
     assert L.iqk_moe_prefill(ctypes.byref(w), vp, None, fake, 1, fake, 0, 6, 0, fake, nb.value, fake, s0) == 0
+    # fused prefill and grouped matvec: routing arrays plus an int64 [E + 1] work plan
+    assert L.iqk_moe_prefill_fused_workspace(ctypes.byref(w), 8, 6, ctypes.byref(nb)) == 0
+    assert nb.value == 256 + 256 + 256 + 256
+    w = _wdesc(K, 4, 64, 2048)
+    assert L.iqk_moe_gemv_grouped_workspace(ctypes.byref(w), 100, 6, ctypes.byref(nb)) == 0
+    assert nb.value == 256 + 256 + 2560 + 256
+    assert L.iqk_moe_gemv_grouped(ctypes.byref(w), vp, None, fake, 2, 1, fake, 100, 6, 0, fake, nb.value - 1, fake,
+                                  s0) == q._E_SIZE
+    assert L.iqk_moe_gemv_grouped(ctypes.byref(w), vp, None, fake, 2, 1, fake, 100, 6, 2, fake, nb.value, fake,
+                                  s0) == q._E_ARG  # sorted flag
+    assert L.iqk_moe_gemv_grouped(ctypes.byref(w), bad_vals.ctypes.data_as(P), None, fake, 2, 1, fake, 100, 6, 0,
+                                  fake, nb.value, fake, s0) == q._E_TABLE
+    assert L.iqk_moe_gemv_grouped(ctypes.byref(w), vp, None, fake, 2, 1, fake, 0, 6, 0, fake, nb.value, fake,
+                                  s0) == 0
+    w = _wdesc(K, 4, 64, 1024)
+    assert L.iqk_moe_gemv_grouped(ctypes.byref(w), vp, None, fake, 2, 1, fake, 1, 6, 0, fake, 1 << 20, fake,
+                                  s0) == q._E_WIDTH
 
 
 def test_python_errors_map_to_exception_types():

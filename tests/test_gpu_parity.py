@@ -231,6 +231,22 @@ def test_route_drops_invalid_ids():
     assert np.array_equal(got[: p0.size], p0) and np.all(got[p0.size:] == -1)
 
 
+def test_route_invalid_ids_across_staging_chunks():
+    """4400 pairs (ids are staged 4096 at a time), invalid ids on both sides
+    of the chunk boundary"""
+    T, k, E = 1100, 4, 37
+    ids = synth.topk_ids(T, k, E, 771)
+    flat = ids.reshape(-1)
+    flat[[5, 4095, 4096, 4097, 4399]] = [-1, E, -7, E + 100, -1]
+    announce("route: invalid ids across staging chunks")
+    counts, offsets, perm = q.route(to_dev(ids), E)
+    c0, o0, p0, bad = oracle.route(ids, E)
+    assert np.array_equal(counts.cpu().numpy(), c0)
+    assert np.array_equal(offsets.cpu().numpy(), o0)
+    got = perm.cpu().numpy()
+    assert np.array_equal(got[: p0.size], p0) and np.all(got[p0.size:] == -1)
+
+
 # ---------------------------------------------------------------------------
 # grouped GEMM and prefill
 # ---------------------------------------------------------------------------
