@@ -83,6 +83,8 @@ def _load():
         "iqk_moe_gemv_combine": (i32, [W, p, p, p, i32, i32, p, p, i64, i32, p, p]),
         "iqk_moe_gemv_grouped_workspace": (i32, [W, i64, i32, p]),
         "iqk_moe_gemv_grouped": (i32, [W, p, p, p, i32, i32, p, i64, i32, i32, p, sz, p, p]),
+        "iqk_moe_auto_workspace": (i32, [W, i64, i32, p]),
+        "iqk_moe_auto": (i32, [W, p, p, p, i32, i32, p, i64, i32, p, sz, p, p, p]),
         "iqk_route": (i32, [p, i64, i64, i32, p, p, p, p]),
         "iqk_grouped_gemm": (i32, [p, i64, i64, i64, p, i32, i64, i32, p, p, p, p]),
         "iqk_moe_prefill_workspace": (i32, [W, i64, i32, p]),
@@ -291,6 +293,32 @@ def moe_gemv_grouped(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=None
                                      _dev(workspace, "workspace", torch.uint8), workspace.numel(),
                                      _dev(y, "y", torch.float32), _stream(stream)))
     return y
+
+
+AUTO_PATHS = ("gemv", "grouped_gemv", "fused_prefill")
+
+
+def moe_auto(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=None, grid: torch.Tensor | None = None,
+             x_slots: int = 1, workspace: torch.Tensor | None = None, y: torch.Tensor | None = None,
+             stream=None) -> tuple[torch.Tensor, str]:
+    """The routed projection with the path picked by pairs per expert
+    (per-pair matvec, grouped matvec or fused prefill); returns (y, path)."""
+    T, k = ids.shape
+    xp, xdt = _x_args(x, T, x_slots, w.in_features)
+    if workspace is None:
+        b = ctypes.c_size_t()
+        cw0 = _Weights(_fmt(w.fmt), w.experts, w.out, w.in_features, None, 0)
+        _check(_lib.iqk_moe_auto_workspace(ctypes.byref(cw0), T, k, ctypes.byref(b)))
+        workspace = torch.empty(b.value, dtype=torch.uint8, device=w.streams.device)
+    if y is None:
+        y = torch.zeros((T, k, w.out), dtype=torch.float32, device=w.streams.device)
+    _v, vp = _host_values(values)
+    cw = w._c()
+    path = ctypes.c_int(-1)
+    _check(_lib.iqk_moe_auto(ctypes.byref(cw), vp, _dev(grid, "grid", torch.int8), xp, xdt, x_slots,
+                             _dev(ids, "ids", torch.int32), T, k, _dev(workspace, "workspace", torch.uint8),
+                             workspace.numel(), _dev(y, "y", torch.float32), ctypes.byref(path), _stream(stream)))
+    return y, AUTO_PATHS[path.value]
 
 
 def floor_gemv(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=None, grid: torch.Tensor | None = None,

@@ -294,6 +294,37 @@ __device__ __forceinline__ void decode_chunk(const DequantParams& p, int64_t row
 #pragma unroll
             for (int i = 0; i < WideShape<OUT_DT>::WORDS; ++i) o[i] = h + (uint32_t)i;
             return;
+        } else if constexpr (OUT_DT != IQK_F32) {
+            // A 32-weight block takes three values, scale * (g + shift) for
+            // g = 0, +1, -1, each rounded once to the output type: a 4-entry
+            // table indexed by the grid byte & 3 (0, 1, 3), split into low and
+            // high bytes so one v_perm_b32 builds a weight pair from a
+            // selector that one more v_perm_b32 makes from the grid bytes.
+            const float df = half_bits_to_float((uint16_t)d);
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const uint32_t h16 = (qh >> (16 * b)) & 0xFFFFu;
+                const float scale = df * (float)(2 * ((h16 >> 12) & 7u) + 1);
+                const float shift = (h16 >> 15) ? -0.125f : 0.125f;
+                const uint32_t p0 = cvt_pair<OUT_DT>(scale * (0.0f + shift), scale * (1.0f + shift));
+                const uint32_t p1 = cvt_pair<OUT_DT>(0.0f, scale * (-1.0f + shift));
+                const uint32_t tlo = __builtin_amdgcn_perm(p1, p0, 0x06040200u);
+                const uint32_t thi = __builtin_amdgcn_perm(p1, p0, 0x07050301u);
+                const uint32_t qsw = b == 0 ? q.x : q.y;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t idx = ((qsw >> (8 * j)) & 0xFFu) | (((h16 >> (3 * j)) & 7u) << 8);
+                    const uint2 gv = grid_s[idx];
+                    const uint32_t vx = gv.x & 0x03030303u, vy = gv.y & 0x03030303u;
+                    const uint32_t vx4 = vx | 0x04040404u, vy4 = vy | 0x04040404u;
+                    // selectors [c_a, 4 + c_a, c_b, 4 + c_b] for the pairs (0, 1) and (2, 3)
+                    o[16 * b + 4 * j + 0] = __builtin_amdgcn_perm(thi, tlo, __builtin_amdgcn_perm(vx4, vx, 0x05010400u));
+                    o[16 * b + 4 * j + 1] = __builtin_amdgcn_perm(thi, tlo, __builtin_amdgcn_perm(vx4, vx, 0x07030602u));
+                    o[16 * b + 4 * j + 2] = __builtin_amdgcn_perm(thi, tlo, __builtin_amdgcn_perm(vy4, vy, 0x05010400u));
+                    o[16 * b + 4 * j + 3] = __builtin_amdgcn_perm(thi, tlo, __builtin_amdgcn_perm(vy4, vy, 0x07030602u));
+                }
+            }
+            return;
         } else {
             const float df = half_bits_to_float((uint16_t)d);
 #pragma unroll

@@ -641,6 +641,35 @@ int iqk_moe_gemv_grouped(const iqk_weights* w, const float* values, const int8_t
     return ok();
 }
 
+int iqk_moe_auto_workspace(const iqk_weights* w, int64_t T, int k, size_t* bytes) {
+    // the grouped matvec and the fused prefill need the same routing arrays and plan
+    return iqk_moe_gemv_grouped_workspace(w, T, k, bytes);
+}
+
+int iqk_moe_auto(const iqk_weights* w, const float* values, const int8_t* grid, const void* x, int x_dtype,
+                 int x_slots, const int32_t* ids, int64_t T, int k, void* workspace, size_t ws_bytes, float* y,
+                 int* path, void* stream) {
+    int rc = check_weights(w);
+    if (rc) return rc;
+    if (T < 0 || k <= 0) return fail(IQK_E_ARG, "T must be >= 0 and k > 0");
+    // measured crossover on the routed geometry (top-6 of 256, in = 2048 / 4096): the
+    // per-pair matvec up to 16 tokens (3/8 pair per expert), the grouped
+    // matvec up to 64 (1.5 pairs per expert), the fused prefill beyond
+    const double per_expert = (double)(T * k) / (double)w->experts;
+    uint32_t lo = 0, hi = 0;
+    float sc = 1.f;
+    const bool int8_table = w->fmt == IQK_IQ1_S_R4 || (values && table_to_int8(values, &lo, &hi, &sc));
+    int choice = per_expert <= 0.375 ? 0 : (per_expert <= 1.5 ? 1 : 2);
+    if (choice == 2 && x_dtype != IQK_BF16) choice = 1;  // the prefill takes bf16 activations
+    if (choice < 2 && !int8_table && x_dtype == IQK_BF16) choice = 2;  // any float table: the prefill
+    if (path) *path = choice;
+    if (choice == 0) return iqk_moe_gemv(w, values, grid, x, x_dtype, x_slots, ids, T, k, y, stream);
+    if (choice == 1)
+        return iqk_moe_gemv_grouped(w, values, grid, x, x_dtype, x_slots, ids, T, k, 0, workspace, ws_bytes, y,
+                                    stream);
+    return iqk_moe_prefill_fused(w, values, grid, x, x_slots, ids, T, k, 0, workspace, ws_bytes, y, stream);
+}
+
 int iqk_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, void* stream) {
     if (!buf || !sink || bytes == 0 || bytes % 16 || sink_words == 0) return fail(IQK_E_ARG, "bad stream-read arguments");
     hipError_t e = iqk::launch_stream_read(buf, bytes, sink, sink_words, (hipStream_t)stream);

@@ -125,7 +125,11 @@ int iqk_unpack_relayout(int fmt, const uint8_t* streams, size_t streams_bytes, i
  * unspecified payload).
  * `values`: host float[8] for the 2-bit members (any float32 values),
  * ignored for IQ1_S_R4.  `grid`: device int8[2048*8] (row idx = 8 grid
- * values) for IQ1_S_R4, ignored otherwise. */
+ * values) for IQ1_S_R4, ignored otherwise; its values are ternary
+ * (-1, 0, +1, the grid's definition): the f16 / bf16 outputs look each
+ * weight up among the three rounded values a block can take, so any other
+ * grid value gives an unspecified result there (float32 output computes
+ * every weight). */
 int iqk_dequant(const iqk_weights* w, int64_t row0, int64_t nrows, const float* values,
                 const int8_t* grid, int out_dtype, void* out, void* stream);
 
@@ -193,6 +197,26 @@ int iqk_moe_gemv_grouped(const iqk_weights* w, const float* values, const int8_t
                          int64_t T, int k, int sorted, void* workspace, size_t ws_bytes,
                          float* y, void* stream);
 
+/* Workspace of iqk_moe_auto (that of iqk_moe_gemv_grouped, which equals
+ * that of iqk_moe_prefill_fused). */
+int iqk_moe_auto_workspace(const iqk_weights* w, int64_t T, int k, size_t* bytes);
+
+/* The routed projection y[T, k, out] with the path chosen by the number of
+ * token-expert pairs ("Surface": few pairs take the fused decode, many the
+ * prefill), with the crossover measured on the routed geometry (top-6 of
+ * 256 experts, in = 2048 and 4096): pairs per expert T*k/E <= 3/8 ->
+ * iqk_moe_gemv; <= 3/2 -> iqk_moe_gemv_grouped; above ->
+ * iqk_moe_prefill_fused.  A float32 activation never takes the prefill
+ * (it needs bf16); a value table that is not int8-exact takes the prefill
+ * when x is bf16 (else IQK_E_TABLE).  *path (if non-null) receives 0, 1 or
+ * 2 for the path taken.  Arguments and errors are those of the chosen call;
+ * accuracy is that call's (1e-3 for the matvecs, 2e-2 for the prefill).  Rows
+ * of pairs with an invalid id are left as they were or set to NaN,
+ * depending on the path. */
+int iqk_moe_auto(const iqk_weights* w, const float* values, const int8_t* grid,
+                 const void* x, int x_dtype, int x_slots, const int32_t* ids, int64_t T, int k,
+                 void* workspace, size_t ws_bytes, float* y, int* path, void* stream);
+
 /* Routing gather ("Surface": sorting pairs by expert so that each expert's
  * weights are read once).  ids: device int32 [P] (P = T*k pair indices
  * t*k + j).  Writes device int32 counts[E], offsets[E+1] (exclusive prefix
@@ -227,8 +251,9 @@ int iqk_moe_prefill_fused_workspace(const iqk_weights* w, int64_t T, int k, size
  * the compressed streams in registers and multiplied with the expert's
  * gathered bf16 token rows, float32 accumulation.  Arguments as
  * iqk_moe_prefill (workspace from iqk_moe_prefill_fused_workspace); the
- * value table may be any float32 values.  Widths: in = 512, 2048 or 4096
- * (IQK_E_WIDTH otherwise); out * iqk_row_bytes(fmt, in) < 2^31.
+ * value table may be any float32 values; the IQ1_S_R4 grid must be
+ * ternary as for iqk_dequant's f16 / bf16 output.  Widths: in = 512, 2048
+ * or 4096 (IQK_E_WIDTH otherwise); out * iqk_row_bytes(fmt, in) < 2^31.
  * Accuracy: as iqk_moe_prefill (2e-2 against the float32-weight product;
  * the result differs from iqk_moe_prefill only in summation order). */
 int iqk_moe_prefill_fused(const iqk_weights* w, const float* values, const int8_t* grid,

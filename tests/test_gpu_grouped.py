@@ -89,3 +89,25 @@ def test_grouped_skewed_routing(fmt):
     y = q.moe_gemv_grouped(w, to_dev(x, torch.bfloat16), to_dev(ids), values, to_dev(grid)).cpu().numpy()
     ref = oracle.moe(fmt, s, E, out, n, x, ids, values, grid)
     assert np.all(rel_err_per_vector(y, ref) <= TOL_GEMV)
+
+
+@pytest.mark.parametrize("T,expect", [(2, "gemv"), (8, "grouped_gemv"), (20, "fused_prefill")])
+def test_auto_dispatch_by_pairs_per_expert(T, expect):
+    """pairs per expert 0.25 / 1 / 2.5 pick the per-pair matvec, the grouped
+    matvec and the fused prefill; each result meets its path's bar"""
+    fmt, n, out, E, k = K, 512, 64, 16, 2
+    seed = 1600 + T
+    w, s = _weights(fmt, E, out, n, seed)
+    values = synth.values_table(seed + 1)
+    x = bf16_round(synth.normal((T, 1, n), seed + 3))
+    ids = synth.topk_ids(T, k, E, seed + 4)
+    announce(f"auto dispatch T={T}")
+    y, path = q.moe_auto(w, to_dev(x, torch.bfloat16), to_dev(ids), values)
+    assert path == expect
+    ref = oracle.moe(fmt, s, E, out, n, x, ids, values)
+    tol = TOL_GEMV if path != "fused_prefill" else 2e-2
+    assert np.all(rel_err_per_vector(y.cpu().numpy(), ref) <= tol)
+    # a float32 activation never takes the prefill
+    y32, path32 = q.moe_auto(w, to_dev(x, torch.float32), to_dev(ids), values)
+    assert path32 == ("gemv" if expect == "gemv" else "grouped_gemv")
+    assert np.all(rel_err_per_vector(y32.cpu().numpy(), ref) <= TOL_GEMV)
