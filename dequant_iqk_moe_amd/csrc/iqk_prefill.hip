@@ -33,6 +33,8 @@ namespace {
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteMaxE = 16384;
 constexpr int kRouteStage = 4096;  // ids staged in LDS per scatter chunk
+constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kRouteHistE = 1024;  // experts up to which the waves rank in parallel
 
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids, int32_t P, int32_t E,
                                                               int32_t* __restrict__ counts,
@@ -41,6 +43,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
     __shared__ int32_t cur[kRouteMaxE];
     __shared__ int32_t part[kRouteThreads];
     __shared__ int32_t stage[kRouteStage];
+    __shared__ int32_t hist[kRouteWaves * kRouteHistE];  // per-wave expert counts, then starts
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += kRouteThreads) cur[e] = 0;
     __syncthreads();
@@ -74,37 +77,69 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
     const int total = part[kRouteThreads - 1];
     // positions past the valid pairs (invalid ids are dropped)
     for (int p = total + tid; p < P; p += kRouteThreads) perm[p] = -1;
-    // stable scatter: the ids are staged in LDS a chunk at a time by the
-    // whole workgroup, then one wave ranks 64 pairs per step (equal ids
-    // found with one ballot per id bit) and advances the cursors
+    // stable scatter.  The ids are staged in LDS a chunk at a time.  Up to
+    // kRouteHistE experts, each wave takes a contiguous slice of the chunk:
+    // per-wave expert counts, an exclusive prefix over the waves gives each
+    // wave its per-expert start, and the waves then rank their slices in
+    // parallel.  Beyond that, one wave ranks the whole chunk.  Ranking: 64
+    // pairs per step, equal ids found with one ballot per id bit.
     int nbits = 1;
     while ((1 << nbits) < E) ++nbits;
-    const uint64_t lt = (1ull << (tid & 63)) - 1ull;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    const bool waves_split = E <= kRouteHistE;
+    // ranks the pairs [i0, i1) of the staged chunk against the cursors cur_w
+    auto rank_slice = [&](int base, int i0, int i1, int32_t* cur_w) {
+        for (int s0 = i0; s0 < i1; s0 += 64) {
+            const int i = s0 + lane;
+            const int e = i < i1 ? stage[i] : -1;
+            const bool valid = e >= 0 && e < E;
+            uint64_t same = __ballot(valid);
+            for (int b = 0; b < nbits; ++b) {
+                const bool bit = valid && ((e >> b) & 1);
+                const uint64_t m = __ballot(bit);
+                same &= bit ? m : ~m;
+            }
+            const int rank = __popcll(same & lt);
+            const int cnt = __popcll(same);
+            int pos = 0;
+            if (valid) pos = cur_w[e] + rank;
+            __builtin_amdgcn_wave_barrier();
+            if (valid && rank == cnt - 1) cur_w[e] = pos + 1;  // last of its expert advances the cursor
+            __builtin_amdgcn_wave_barrier();
+            if (valid) perm[pos] = base + i;
+        }
+    };
     for (int base = 0; base < P; base += kRouteStage) {
         const int n = min(kRouteStage, P - base);
         __syncthreads();  // the cursors are final / the previous chunk is ranked
         for (int i = tid; i < n; i += kRouteThreads) stage[i] = ids[base + i];
+        if (waves_split)
+            for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) hist[i] = 0;
         __syncthreads();
-        if (tid < 64) {
-            for (int s0 = 0; s0 < n; s0 += 64) {
-                const int i = s0 + tid;
-                const int e = i < n ? stage[i] : -1;
-                const bool valid = e >= 0 && e < E;
-                uint64_t same = __ballot(valid);
-                for (int b = 0; b < nbits; ++b) {
-                    const bool bit = valid && ((e >> b) & 1);
-                    const uint64_t m = __ballot(bit);
-                    same &= bit ? m : ~m;
-                }
-                const int rank = __popcll(same & lt);
-                const int cnt = __popcll(same);
-                int pos = 0;
-                if (valid) pos = cur[e] + rank;
-                __builtin_amdgcn_wave_barrier();
-                if (valid && rank == cnt - 1) cur[e] = pos + 1;  // last of its expert advances the cursor
-                __builtin_amdgcn_wave_barrier();
-                if (valid) perm[pos] = base + i;
+        if (waves_split) {
+            const int per = (n + kRouteWaves - 1) / kRouteWaves;
+            const int i0 = min(wave * per, n), i1 = min(i0 + per, n);
+            for (int i = i0 + lane; i < i1; i += 64) {
+                const int e = stage[i];
+                if (e >= 0 && e < E) atomicAdd(&hist[wave * E + e], 1);
             }
+            __syncthreads();
+            // hist[w][e] <- start of wave w's pairs of expert e; cur[e] advances past the chunk
+            for (int e = tid; e < E; e += kRouteThreads) {
+                int run = cur[e];
+                for (int w = 0; w < kRouteWaves; ++w) {
+                    const int c = hist[w * E + e];
+                    hist[w * E + e] = run;
+                    run += c;
+                }
+                cur[e] = run;
+            }
+            __syncthreads();
+            rank_slice(base, i0, i1, hist + wave * E);
+        } else if (tid < 64) {
+            rank_slice(base, 0, n, cur);
         }
     }
 }
