@@ -71,6 +71,38 @@ def wire(fmt: int, rows: int, n: int, seed: int, sigma: float = 0.01) -> np.ndar
     return w
 
 
+def _scale_mask(fmt: int, rows: int, n: int) -> np.ndarray:
+    """bool [rows * row_bytes]: the bytes that hold fp16 scales in the wire"""
+    rb = row_bytes(fmt, n)
+    m = np.zeros(rows * rb, bool)
+    if fmt == IQ2_KS:
+        v = m.reshape(rows, rb)
+        v[:, 0:2] = True
+    elif fmt == IQ2_K:
+        v = m.reshape(rows * n // 256, 76)
+        v[:, 0:2] = True
+    else:
+        v = m.reshape(rows // 4, 4 * rb)
+        v[:, 0:8] = True
+    return m
+
+
+def wire_experts(fmt: int, E: int, out: int, n: int, seed: int, sigma: float = 0.01) -> np.ndarray:
+    """Stand-in wire of E stacked [out, n] experts built cheaply at full size:
+    one expert drawn as `wire`, and expert e a copy whose non-scale bytes are
+    XORed with a byte of its own (every expert distinct, bytes still uniform,
+    scales unchanged)."""
+    base = wire(fmt, out, n, seed, sigma)
+    keep = _scale_mask(fmt, out, n)
+    pat = np.where(keep, 0, 1).astype(np.uint8)
+    salt = _rng(seed + 1).integers(1, 256, size=E).astype(np.uint8)
+    salt[0] = 0
+    w = np.empty((E, base.size), np.uint8)
+    for e in range(E):
+        np.bitwise_xor(base, pat * salt[e], out=w[e])
+    return w.reshape(-1)
+
+
 def values_table(seed: int) -> np.ndarray:
     """Eight integers in [-32, 31] as float32: a stand-in for the 8-entry
     value table (two 4-entry alphabets), exact in fp16 and bf16."""
