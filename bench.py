@@ -234,16 +234,21 @@ def decode_cell(ctx, pool, T, proj, S, reps, warm, seed):
     def run_floor(i):
         q.floor_gemv(pool.w[i % POOLS], x, ids[i], ctx.values, grid, x_slots=slots, sink=sink)
 
-    ms = timed_graph(torch, run, S, reps, warm)
-    ms_floor = timed_graph(torch, run_floor, S, reps, warm)
+    # decode and floor arms alternate (A B A B A B); medians
+    arms = {"decode": [], "floor": []}
+    for _ in range(3):
+        arms["decode"].append(timed_graph(torch, run, S, reps, warm))
+        arms["floor"].append(timed_graph(torch, run_floor, S, reps, warm))
+    ms, ms_floor = float(np.median(arms["decode"])), float(np.median(arms["floor"]))
     nbytes = float(np.mean([pool.bytes_for(a) for a in ids_host])) + x.numel() * 2 + y.numel() * 4
     ms_stream = ctx.stream_ms(nbytes, S, reps, warm)
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"cell": f"{FMT_NAME[pool.fmt]} {proj} T={T}", "kind": "decode", "us": round(ms * 1e3, 3),
             "bytes": int(nbytes), "GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
             "floor_us": round(ms_floor * 1e3, 3), "ratio_to_floor": round(ms / ms_floor, 3),
-            "stream_read_us": round(ms_stream * 1e3, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
-            "validation_worst": worst}
+            "stream_read_us": round(ms_stream * 1e3, 3),
+            "floor_rate_vs_stream": round(ms_stream / ms_floor, 3),
+            "tokens_per_s": round(T / (ms * 1e-3), 1), "validation_worst": worst}
 
 
 def prefill_cells(ctx, fmt, seed):
@@ -362,21 +367,27 @@ def measured_traffic():
 
 def pmc_launches(torch, q, synth, seed):
     """The headline gate/up matvec (IQ2_K, T=1) 64 times over rotating pools and
-    fresh ids, then the calibration kernels: iqk_stream_read of exactly
-    256 MiB (reads) and a 256 MiB fill (writes), 8 times each."""
+    fresh ids, its deleted-decode floor on the same 64 launches, then the
+    calibration kernels: iqk_stream_read of exactly 256 MiB (reads) and a
+    256 MiB fill (writes), 8 times each."""
     gate_up = Pools(q, torch, q.IQ2_K, 2 * I, H, seed)
     values = synth.values_table(seed + 1)
     x = torch.from_numpy(synth.normal((1, H), seed + 2)).to(torch.bfloat16).cuda()
     y = torch.empty((1, K, 2 * I), dtype=torch.float32, device="cuda")
     ids = [torch.from_numpy(synth.topk_ids(1, K, E, 10_000 + i)).cuda() for i in range(64)]
+    sink = torch.empty((1, K, 2 * I), dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
     for i in range(64):
         q.moe_gemv(gate_up.w[i % POOLS], x, ids[i], values, y=y)
     torch.cuda.synchronize()
+    # the deleted-decode floor on the same launches (its HBM bytes must match the decode's)
+    for i in range(64):
+        q.floor_gemv(gate_up.w[i % POOLS], x, ids[i], values, sink=sink)
+    torch.cuda.synchronize()
     buf = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
-    sink = torch.zeros(1 << 14, dtype=torch.int32, device="cuda")
+    ssink = torch.zeros(1 << 14, dtype=torch.int32, device="cuda")
     for _ in range(8):
-        q.stream_read(buf, sink)
+        q.stream_read(buf, ssink)
     for _ in range(8):
         buf.fill_(3)
     torch.cuda.synchronize()
