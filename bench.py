@@ -63,6 +63,20 @@ def _parse():
     return ap.parse_args()
 
 
+def _host_cpu():
+    """CPU model and logical core count of the host the baseline ran on"""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "logical_cores": os.cpu_count()}
+
+
 def log(msg):
     sys.stderr.write(msg + "\n")
     sys.stderr.flush()
@@ -582,7 +596,8 @@ def main():
         dt = time.perf_counter() - t1
         cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": f"{nsteps} full decode steps (T=1: gate/up and down matvecs of 6 experts each) "
-                         f"through the single-threaded C oracle in {dt:.1f} s"}
+                         f"through the single-threaded C oracle in {dt:.1f} s",
+               "host": _host_cpu()}
 
     result = {
         "metric": "routed-expert decode GB/s and ratio to HBM floor per format/projection",
