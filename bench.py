@@ -343,6 +343,7 @@ def prefill_cells(ctx, fmt, seed):
                     "us": round(fused_ms * 1e3, 1), "bytes": int(fbytes),
                     "GBps": round(fbytes / (fused_ms * 1e-3) / 1e9, 1),
                     "TFLOPs": round(flops / (fused_ms * 1e-3) / 1e12, 2),
+                    "mfma_util": round(flops / (fused_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                     "weights_per_s": round(E * rows * n / (fused_ms * 1e-3), 1),
                     "max_rel_diff_vs_two_pass": fused_vs_two_pass})
         fused_total_ms += fused_ms

@@ -93,9 +93,10 @@ def test_grouped_skewed_routing(fmt):
 
 @pytest.mark.parametrize("T,expect", [(2, "gemv"), (8, "grouped_gemv"), (20, "fused_prefill")])
 def test_auto_dispatch_by_pairs_per_expert(T, expect):
-    """pairs per expert 0.25 / 1 / 2.5 pick the per-pair matvec, the grouped
-    matvec and the fused prefill; each result meets its path's bar"""
-    fmt, n, out, E, k = K, 512, 64, 16, 2
+    """in = 4096: pairs per expert 0.25 / 1 / 2.5 pick the per-pair matvec,
+    the grouped matvec and the fused prefill; each result meets its path's
+    bar"""
+    fmt, n, out, E, k = K, 4096, 64, 16, 2
     seed = 1600 + T
     w, s = _weights(fmt, E, out, n, seed)
     values = synth.values_table(seed + 1)
@@ -111,3 +112,20 @@ def test_auto_dispatch_by_pairs_per_expert(T, expect):
     y32, path32 = q.moe_auto(w, to_dev(x, torch.float32), to_dev(ids), values)
     assert path32 == ("gemv" if expect == "gemv" else "grouped_gemv")
     assert np.all(rel_err_per_vector(y32.cpu().numpy(), ref) <= TOL_GEMV)
+
+
+
+def test_auto_dispatch_narrow_input():
+    """in = 2048: per-pair matvec up to 3/4 pair per expert, then the fused prefill"""
+    fmt, n, out, E, k = KS, 2048, 48, 16, 2
+    w, s = _weights(fmt, E, out, n, 1700)
+    values = synth.values_table(1701)
+    for T, expect in ((6, "gemv"), (8, "fused_prefill")):
+        x = bf16_round(synth.normal((T, 1, n), 1702 + T))
+        ids = synth.topk_ids(T, k, E, 1710 + T)
+        announce(f"auto dispatch narrow T={T}")
+        y, path = q.moe_auto(w, to_dev(x, torch.bfloat16), to_dev(ids), values)
+        assert path == expect
+        ref = oracle.moe(fmt, s, E, out, n, x, ids, values)
+        tol = TOL_GEMV if path == "gemv" else 2e-2
+        assert np.all(rel_err_per_vector(y.cpu().numpy(), ref) <= tol)
