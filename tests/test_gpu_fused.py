@@ -91,3 +91,20 @@ def test_fused_prefill_skewed_routing(fmt):
     y = q.moe_prefill_fused(w, to_dev(x, torch.bfloat16), to_dev(ids), values, to_dev(grid)).cpu().numpy()
     ref_b = oracle.moe(fmt, s, E, out, n, x, ids, values, grid, w_bf16=True)
     assert np.all(rel_err_per_vector(y, ref_b) <= TOL_SAME_WEIGHTS)
+
+
+
+@pytest.mark.parametrize("fmt", [KS, R4])
+def test_fused_prefill_many_experts(fmt):
+    """1500 experts: the work plan scans them in two chunks, the routing ranks
+    with one wave"""
+    n, out, E, T, k = 512, 16, 1500, 300, 6
+    seed = 1800 + fmt
+    announce(f"fused prefill many experts fmt={fmt}")
+    w, s = _weights(fmt, E, out, n, seed)
+    values, grid = synth.values_table(seed + 1), synth.ternary_grid(seed + 2)
+    x = bf16_round(synth.normal((T, 1, n), seed + 3))
+    ids = synth.topk_ids(T, k, E, seed + 4)
+    y = q.moe_prefill_fused(w, to_dev(x, torch.bfloat16), to_dev(ids), values, to_dev(grid)).cpu().numpy()
+    ref_b = oracle.moe(fmt, s, E, out, n, x, ids, values, grid, w_bf16=True)
+    assert np.all(rel_err_per_vector(y, ref_b) <= TOL_SAME_WEIGHTS)

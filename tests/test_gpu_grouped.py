@@ -129,3 +129,19 @@ def test_auto_dispatch_narrow_input():
         ref = oracle.moe(fmt, s, E, out, n, x, ids, values)
         tol = TOL_GEMV if path == "gemv" else 2e-2
         assert np.all(rel_err_per_vector(y.cpu().numpy(), ref) <= tol)
+
+
+
+@pytest.mark.parametrize("fmt", [K, R4])
+def test_grouped_many_experts(fmt):
+    """1500 experts: the plan scans them in two chunks"""
+    n, out, E, T, k = 512, 16, 1500, 300, 6
+    seed = 1900 + fmt
+    announce(f"grouped gemv many experts fmt={fmt}")
+    w, s = _weights(fmt, E, out, n, seed)
+    values, grid = synth.values_table(seed + 1), synth.ternary_grid(seed + 2)
+    x = bf16_round(synth.normal((T, 1, n), seed + 3))
+    ids = synth.topk_ids(T, k, E, seed + 4)
+    y = q.moe_gemv_grouped(w, to_dev(x, torch.bfloat16), to_dev(ids), values, to_dev(grid)).cpu().numpy()
+    ref = oracle.moe(fmt, s, E, out, n, x, ids, values, grid)
+    assert np.all(rel_err_per_vector(y, ref) <= TOL_GEMV)

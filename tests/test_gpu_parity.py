@@ -206,7 +206,8 @@ def test_gemv_activation_outliers_and_zeros():
 # routing gather: bit-exact
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("T,k,E", [(1, 6, 256), (8, 6, 256), (512, 6, 256), (37, 3, 5), (3000, 8, 1000)])
+@pytest.mark.parametrize("T,k,E", [(1, 6, 256), (8, 6, 256), (512, 6, 256), (37, 3, 5), (3000, 8, 1000),
+                                   (700, 8, 3000)])   # more than 1024 experts: one wave ranks
 def test_route_bit_exact(T, k, E):
     ids = synth.topk_ids(T, k, E, 700 + T)
     announce(f"route T={T} k={k} E={E}")
