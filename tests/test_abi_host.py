@@ -160,3 +160,16 @@ def test_python_errors_map_to_exception_types():
         q.pack_relayout(R4, np.zeros(3 * 98, np.uint8), 3, 512)
     with pytest.raises(q.IqkValueError):
         q.plane_offsets(KS, 4, 100)
+
+
+def test_package_refuses_to_import_without_the_library(tmp_path):
+    """no CPU fallback: a copy of the package without libiqk.so fails to import"""
+    import shutil
+    import subprocess
+    import sys
+    src = os.path.dirname(q.__file__)
+    dst = tmp_path / "dequant_iqk_moe_amd"
+    shutil.copytree(src, dst, ignore=shutil.ignore_patterns("*.so", "_build", "__pycache__"))
+    r = subprocess.run([sys.executable, "-c", "import dequant_iqk_moe_amd"], cwd=tmp_path, capture_output=True,
+                       text=True, env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode != 0 and "ImportError" in r.stderr and "not built" in r.stderr
