@@ -23,6 +23,8 @@ Pins used here, none of which re-types the oracle's own formula:
     gives the IEEE result of (d*s)*v, which differs from d*(s*v) on some of
     the sampled cases.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -37,14 +39,15 @@ KS, K, R4 = oracle.IQ2_KS, oracle.IQ2_K, oracle.IQ1_S_R4
 # --------------------------------------------------------------------------
 
 def test_row_budgets_and_bits_per_weight():
-    # literals from the "Format" section budgets at the routed widths
-    assert [oracle.row_bytes(KS, n) for n in (256, 512, 2048, 4096)] == [72, 142, 562, 1122]
-    assert [oracle.row_bytes(K, n) for n in (256, 512, 2048, 4096)] == [76, 152, 608, 1216]
-    assert [oracle.row_bytes(R4, n) for n in (256, 512, 2048, 4096)] == [50, 98, 386, 770]
-    for n in (256, 512, 2048, 4096):
-        assert (oracle.row_bytes(KS, n) * 8 - 16) / n == 2.1875
-        assert oracle.row_bytes(K, n) * 8 / n == 2.375
-        assert (oracle.row_bytes(R4, n) * 8 - 16) / n == 1.5
+    # the pages' budgets and bits per weight (tests/golden/format_budgets.txt, cited there)
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "format_budgets.txt")
+    members = {"IQ2_KS": KS, "IQ2_K": K, "IQ1_S_R4": R4}
+    rows = [l.split() for l in open(path) if l.strip() and not l.startswith("#")]
+    assert len(rows) == 12
+    for name, n, rb, scale_bits, bpw in rows:
+        fmt, n, rb = members[name], int(n), int(rb)
+        assert oracle.row_bytes(fmt, n) == rb
+        assert (rb * 8 - int(scale_bits)) / n == float(bpw)
     # invalid shapes are refused
     assert oracle.row_bytes(KS, 100) == -1
     assert oracle.tensor_bytes(R4, 6, 256) == -1
