@@ -88,9 +88,8 @@ class Pools:
     def __init__(self, q, torch, fmt, out, n, seed, pools=POOLS):
         import synth
         wire = synth.wire(fmt, E * out, n, seed)
-        streams = q.pack_relayout(fmt, wire, E * out, n)
-        self.host_streams = streams
-        base = torch.from_numpy(streams).cuda()
+        self.wire = wire  # the oracle packs what it needs from the wire itself
+        base = torch.from_numpy(q.pack_relayout(fmt, wire, E * out, n)).cuda()
         self.w = [q.Weights(fmt, E, out, n, base)] + [q.Weights(fmt, E, out, n, base.clone()) for _ in range(pools - 1)]
         self.fmt, self.out, self.n = fmt, out, n
         self.row_bytes = q.row_bytes(fmt, n)
@@ -167,6 +166,32 @@ class Ctx:
         return timed_graph(self.torch, sread, S, reps, warm)
 
 
+def oracle_row(oracle, fmt, wire, out, n, e, r, values, grid_host, dtype=None):
+    """row r of expert e reconstructed by the oracle from its own packing of
+    the wire (IQ1_S_R4: the row's four-row group)"""
+    import synth
+    rb = synth.row_bytes(fmt, n)
+    R = e * out + r
+    g = 4 if fmt == 3 else 1
+    r0 = R - R % g
+    s = oracle.pack(fmt, wire[r0 * rb:(r0 + g) * rb], g, n)
+    return oracle.dequant(fmt, s, g, n, values, grid_host, oracle.F32 if dtype is None else dtype,
+                          r0=R - r0, nr=1)[0]
+
+
+def oracle_moe_subset(oracle, fmt, wire, out, n, x, ids, values, grid_host=None, x_slots=1):
+    """the oracle's routed product over only the selected experts, packed by
+    the oracle from the wire (ids remapped onto the subset)"""
+    import synth
+    rb = synth.row_bytes(fmt, n)
+    experts = sorted(set(int(e) for e in np.asarray(ids).ravel()))
+    remap = {e: i for i, e in enumerate(experts)}
+    ids2 = np.vectorize(remap.get)(np.asarray(ids)).astype(np.int32)
+    sub = np.concatenate([wire[e * out * rb:(e + 1) * out * rb] for e in experts])
+    streams = oracle.pack(fmt, sub, len(experts) * out, n)
+    return oracle.moe(fmt, streams, len(experts), out, n, x, ids2, values, grid_host, x_slots=x_slots)
+
+
 def validate_sample(oracle, pool, ids, xin, y, slots, values, grid_host, rng, rows_per=48):
     """worst |y - y_exact| / sum|w x| over sampled rows of every selected expert"""
     worst = 0.0
@@ -176,8 +201,8 @@ def validate_sample(oracle, pool, ids, xin, y, slots, values, grid_host, rng, ro
         for j in range(k):
             e = int(ids[t, j])
             for r in rng.choice(pool.out, rows_per, replace=False):
-                w = oracle.dequant(pool.fmt, pool.host_streams, E * pool.out, pool.n, values, grid_host,
-                                   oracle.F32, r0=e * pool.out + int(r), nr=1)[0].astype(np.float64)
+                w = oracle_row(oracle, pool.fmt, pool.wire, pool.out, pool.n, e, int(r), values,
+                               grid_host).astype(np.float64)
                 xx = (xin[t, 0] if slots == 1 else xin[t, j]).astype(np.float64)
                 ref = float(w @ xx)
                 scale = float(np.abs(w) @ np.abs(xx))
@@ -203,11 +228,11 @@ def layer_cell(ctx, gate_up, down, x, S, reps, warm, seed):
     q.moe_gemv_combine(down.w[0], hbuf, ids[0], rw, ctx.values, y=y)
     torch.cuda.synchronize()
     xv = x.float().cpu().numpy().reshape(T, 1, H)
-    gu = oracle.moe(q.IQ2_K, gate_up.host_streams, E, 2 * I, H, xv, ids_host[0], ctx.values)
+    gu = oracle_moe_subset(oracle, q.IQ2_K, gate_up.wire, 2 * I, H, xv, ids_host[0], ctx.values)
     h_ref = oracle.swiglu(gu)
     h_gpu = hbuf.float().cpu().numpy()
     err_h = float(np.max(np.linalg.norm(h_gpu - h_ref, axis=-1) / np.linalg.norm(h_ref, axis=-1)))
-    parts = oracle.moe(q.IQ2_K, down.host_streams, E, H, I, h_gpu, ids_host[0], ctx.values, x_slots=K)
+    parts = oracle_moe_subset(oracle, q.IQ2_K, down.wire, H, I, h_gpu, ids_host[0], ctx.values, x_slots=K)
     y_ref = oracle.combine(parts, rw_host)
     scale = np.sum(np.abs(rw_host)[:, :, None] * np.linalg.norm(parts, axis=-1, keepdims=True), axis=1)[:, 0]
     err_y = float(np.max(np.linalg.norm(y.cpu().numpy() - y_ref, axis=-1) / scale))
@@ -283,9 +308,7 @@ def prefill_cells(ctx, fmt, seed):
     for proj, (rows, n) in (("gate_up", (2 * I, H)), ("down", (H, I))):
         slots = 1 if proj == "gate_up" else K
         wire = synth.wire(fmt, E * rows, n, seed + (1 if proj == "gate_up" else 2))
-        streams_h = q.pack_relayout(fmt, wire, E * rows, n)
-        del wire
-        w = q.Weights(fmt, E, rows, n, torch.from_numpy(streams_h).cuda())
+        w = q.Weights(fmt, E, rows, n, torch.from_numpy(q.pack_relayout(fmt, wire, E * rows, n)).cuda())
         dense = torch.empty((E, rows, n), dtype=torch.bfloat16, device="cuda")
         x = torch.from_numpy(synth.normal((T, slots, n), seed + 5)).to(torch.bfloat16).cuda()
         y = torch.zeros((T, K, rows), dtype=torch.float32, device="cuda")
@@ -301,8 +324,7 @@ def prefill_cells(ctx, fmt, seed):
             t, j = int(rng.integers(T)), int(rng.integers(K))
             e = int(ids_h[t, j])
             r = int(rng.integers(rows))
-            wr = oracle.dequant(fmt, streams_h, E * rows, n, ctx.values, ctx.grid_host, oracle.F32,
-                                r0=e * rows + r, nr=1)[0].astype(np.float64)
+            wr = oracle_row(oracle, fmt, wire, rows, n, e, r, ctx.values, ctx.grid_host).astype(np.float64)
             xx = (xv[t, 0] if slots == 1 else xv[t, j]).astype(np.float64)
             worst = max(worst, abs(float(yv[t, j, r]) - float(wr @ xx)) / max(float(np.abs(wr) @ np.abs(xx)), 1e-30))
         wbytes = E * rows * q.row_bytes(fmt, n)
@@ -354,6 +376,67 @@ def prefill_cells(ctx, fmt, seed):
     out.append({"cell": f"{FMT_NAME[fmt]} prefill total fused (2 x (route + fused GEMM))", "kind": "prefill",
                 "us": round(fused_total_ms * 1e3, 1), "tokens_per_s": round(T / (fused_total_ms * 1e-3), 1)})
     return out
+
+
+def prefill_layer_cell(ctx, seed):
+    """One MoE layer's routed experts at 512 tokens through the fused
+    prefill: gate/up (route + fused GEMM), SwiGLU to bf16 h, down (route +
+    fused GEMM) and the router-weighted combine to y [512, hidden].  Two
+    sampled tokens are checked against the oracle chain first."""
+    import synth
+    import oracle
+    q, torch = ctx.q, ctx.torch
+    T, fmt = 512, q.IQ2_K
+    wgu = synth.wire(fmt, E * 2 * I, H, seed + 1)
+    wdn = synth.wire(fmt, E * H, I, seed + 2)
+    gu = q.Weights(fmt, E, 2 * I, H, torch.from_numpy(q.pack_relayout(fmt, wgu, E * 2 * I, H)).cuda())
+    dn = q.Weights(fmt, E, H, I, torch.from_numpy(q.pack_relayout(fmt, wdn, E * H, I)).cuda())
+    ids_h = synth.topk_ids(T, K, E, seed + 3)
+    ids = torch.from_numpy(ids_h).cuda()
+    rw_h = np.random.default_rng(seed + 4).dirichlet(np.ones(K), size=T).astype(np.float32)
+    rw = torch.from_numpy(rw_h).cuda()
+    x = torch.from_numpy(synth.normal((T, 1, H), seed + 5)).to(torch.bfloat16).cuda()
+    ws = torch.empty(q.prefill_fused_workspace_bytes(gu, T, K), dtype=torch.uint8, device="cuda")
+    y_gu = torch.empty((T, K, 2 * I), dtype=torch.float32, device="cuda")
+    h = torch.empty((T, K, I), dtype=torch.bfloat16, device="cuda")
+    y_dn = torch.empty((T, K, H), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+
+    def run(i):
+        q.moe_prefill_fused(gu, x, ids, ctx.values, workspace=ws, y=y_gu)
+        q.swiglu(y_gu, h=h)
+        q.moe_prefill_fused(dn, h, ids, ctx.values, x_slots=K, workspace=ws, y=y_dn)
+        q.combine(y_dn, rw, yc=y)
+
+    run(0)
+    torch.cuda.synchronize()
+    # the oracle chain on two tokens (bf16 weights, as the prefill multiplies with)
+    worst_h, worst_y = 0.0, 0.0
+    for t in (3, 300):
+        xt = x[t:t + 1].float().cpu().numpy()
+        sel = ids_h[t:t + 1]
+        experts = sorted(set(int(e) for e in sel.ravel()))
+        remap = {e: j for j, e in enumerate(experts)}
+        sel2 = np.vectorize(remap.get)(sel).astype(np.int32)
+        rbg, rbd = q.row_bytes(fmt, H), q.row_bytes(fmt, I)
+        sg = oracle.pack(fmt, np.concatenate([wgu[e * 2 * I * rbg:(e + 1) * 2 * I * rbg] for e in experts]),
+                         len(experts) * 2 * I, H)
+        sd = oracle.pack(fmt, np.concatenate([wdn[e * H * rbd:(e + 1) * H * rbd] for e in experts]),
+                         len(experts) * H, I)
+        h_ref = oracle.swiglu(oracle.moe(fmt, sg, len(experts), 2 * I, H, xt, sel2, ctx.values, w_bf16=True))
+        h_gpu = h[t:t + 1].float().cpu().numpy()
+        worst_h = max(worst_h, float(np.max(np.linalg.norm(h_gpu - h_ref, axis=-1) /
+                                            np.linalg.norm(h_ref, axis=-1))))
+        parts = oracle.moe(fmt, sd, len(experts), H, I, h_gpu, sel2, ctx.values, x_slots=K, w_bf16=True)
+        y_ref = oracle.combine(parts, rw_h[t:t + 1])
+        scale = float(np.sum(np.abs(rw_h[t]) * np.linalg.norm(parts[0], axis=-1)))
+        worst_y = max(worst_y, float(np.linalg.norm(y[t].cpu().numpy() - y_ref[0]) / scale))
+    ms = timed_eager(torch, run, 10, 2)
+    del gu, dn, ws, y_gu, h, y_dn, y
+    torch.cuda.empty_cache()
+    return {"cell": "IQ2_K MoE layer T=512 prefill: fused gate/up, SwiGLU, fused down, combine", "kind": "prefill",
+            "us": round(ms * 1e3, 1), "tokens_per_s": round(T / (ms * 1e-3), 1), "validation_h": worst_h,
+            "validation_y": worst_y}
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_iqk2k_gate_up_t1_traffic.md")
@@ -580,21 +663,32 @@ def main():
         torch.cuda.empty_cache()
         for fmt in (q.IQ2_K, q.IQ2_KS, q.IQ1_S_R4):
             cells.extend(prefill_cells(ctx, fmt, 500 + fmt))
+        cells.append(prefill_layer_cell(ctx, 600))
     for c in cells:
         log(json.dumps(c))
 
     cpu = None
     if not args.no_cpu_baseline:
         # whole decode steps through the single-threaded oracle, about 10 s of CPU work
-        t1 = time.perf_counter()
+        # (the oracle packs each step's experts from the wire first, untimed)
+        dt = 0.0
         nsteps, nbytes = 0, 0
-        while nsteps < 1 or (time.perf_counter() - t1 < 10.0 and nsteps < len(ids_host)):
+        while nsteps < 1 or (dt < 10.0 and nsteps < len(ids_host)):
             a = ids_host[nsteps]
-            oracle.moe(q.IQ2_K, gate_up.host_streams, E, 2 * I, H, xv, a, values)
-            oracle.moe(q.IQ2_K, down.host_streams, E, H, I, hv, a, values, x_slots=K)
+            steps = []
+            for pool, xin, slots in ((gate_up, xv, 1), (down, hv, K)):
+                experts = sorted(set(int(e) for e in a.ravel()))
+                remap = {e: i for i, e in enumerate(experts)}
+                rb = q.row_bytes(pool.fmt, pool.n)
+                sub = np.concatenate([pool.wire[e * pool.out * rb:(e + 1) * pool.out * rb] for e in experts])
+                steps.append((oracle.pack(pool.fmt, sub, len(experts) * pool.out, pool.n), len(experts), pool,
+                              xin, np.vectorize(remap.get)(a).astype(np.int32), slots))
+            t1 = time.perf_counter()
+            for streams, ne, pool, xin, ids2, slots in steps:
+                oracle.moe(q.IQ2_K, streams, ne, pool.out, pool.n, xin, ids2, values, x_slots=slots)
+            dt += time.perf_counter() - t1
             nbytes += bytes_steps[nsteps]
             nsteps += 1
-        dt = time.perf_counter() - t1
         cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": f"{nsteps} full decode steps (T=1: gate/up and down matvecs of 6 experts each) "
                          f"through the single-threaded C oracle in {dt:.1f} s",

@@ -85,6 +85,8 @@ def _load():
         "iqk_moe_gemv_grouped": (i32, [W, p, p, p, i32, i32, p, i64, i32, i32, p, sz, p, p]),
         "iqk_moe_auto_workspace": (i32, [W, i64, i32, p]),
         "iqk_moe_auto": (i32, [W, p, p, p, i32, i32, p, i64, i32, p, sz, p, p, p]),
+        "iqk_swiglu": (i32, [p, i64, i64, p, p]),
+        "iqk_combine": (i32, [p, p, i64, i32, i64, p, p]),
         "iqk_route": (i32, [p, i64, i64, i32, p, p, p, p]),
         "iqk_grouped_gemm": (i32, [p, i64, i64, i64, p, i32, i64, i32, p, p, p, p]),
         "iqk_moe_prefill_workspace": (i32, [W, i64, i32, p]),
@@ -293,6 +295,29 @@ def moe_gemv_grouped(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=None
                                      _dev(workspace, "workspace", torch.uint8), workspace.numel(),
                                      _dev(y, "y", torch.float32), _stream(stream)))
     return y
+
+
+def swiglu(y_gu: torch.Tensor, h: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """h = silu(gate) * up (bf16) from a gate/up projection's output
+    y_gu [..., 2I] (float32; gate columns first)."""
+    if y_gu.dtype != torch.float32 or y_gu.shape[-1] % 2:
+        raise IqkValueError(_E_ARG, "y_gu must be float32 [..., 2I]")
+    I = y_gu.shape[-1] // 2
+    P = y_gu.numel() // (2 * I)
+    if h is None:
+        h = torch.empty((*y_gu.shape[:-1], I), dtype=torch.bfloat16, device=y_gu.device)
+    _check(_lib.iqk_swiglu(_dev(y_gu, "y_gu", torch.float32), P, I, _dev(h, "h", torch.bfloat16), _stream(stream)))
+    return h
+
+
+def combine(y: torch.Tensor, route_w: torch.Tensor, yc: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """yc[t] = sum_j route_w[t, j] * y[t, j] (float32, slot order) from y [T, k, out]."""
+    T, k, out = y.shape
+    if yc is None:
+        yc = torch.empty((T, out), dtype=torch.float32, device=y.device)
+    _check(_lib.iqk_combine(_dev(y, "y", torch.float32), _dev(route_w, "route_w", torch.float32), T, k, out,
+                            _dev(yc, "yc", torch.float32), _stream(stream)))
+    return yc
 
 
 AUTO_PATHS = ("gemv", "grouped_gemv", "fused_prefill")

@@ -25,6 +25,7 @@ PER_FILE = {
     "iqk_gemv.hip": [],
     "iqk_prefill.hip": [],
     "iqk_fused.hip": [],
+    "iqk_glue.hip": [],
     "iqk_host.cpp": [],
 }
 

@@ -674,6 +674,28 @@ int iqk_moe_auto(const iqk_weights* w, const float* values, const int8_t* grid, 
     return iqk_moe_prefill_fused(w, values, grid, x, x_slots, ids, T, k, 0, workspace, ws_bytes, y, stream);
 }
 
+int iqk_swiglu(const float* y_gu, int64_t P, int64_t I, uint16_t* h, void* stream) {
+    if (P < 0 || I <= 0) return fail(IQK_E_ARG, "bad sizes");
+    if (I % 4) return fail(IQK_E_SHAPE, "SwiGLU needs I %% 4 == 0 (I = %lld)", (long long)I);
+    if (P == 0) return ok();
+    if (!y_gu || !h) return fail(IQK_E_ARG, "null pointer");
+    if ((uintptr_t)y_gu % 16 || (uintptr_t)h % 8) return fail(IQK_E_ARG, "y_gu must be 16-byte and h 8-byte aligned");
+    hipError_t e = iqk::launch_swiglu(y_gu, P, I, h, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "SwiGLU launch");
+    return ok();
+}
+
+int iqk_combine(const float* y, const float* route_w, int64_t T, int k, int64_t out, float* yc, void* stream) {
+    if (T < 0 || k <= 0 || out <= 0) return fail(IQK_E_ARG, "bad sizes");
+    if (out % 4) return fail(IQK_E_SHAPE, "combine needs out %% 4 == 0 (out = %lld)", (long long)out);
+    if (T == 0) return ok();
+    if (!y || !route_w || !yc) return fail(IQK_E_ARG, "null pointer");
+    if ((uintptr_t)y % 16 || (uintptr_t)yc % 16) return fail(IQK_E_ARG, "y and yc must be 16-byte aligned");
+    hipError_t e = iqk::launch_combine(y, route_w, T, k, out, yc, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    return ok();
+}
+
 int iqk_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, void* stream) {
     if (!buf || !sink || bytes == 0 || bytes % 16 || sink_words == 0) return fail(IQK_E_ARG, "bad stream-read arguments");
     hipError_t e = iqk::launch_stream_read(buf, bytes, sink, sink_words, (hipStream_t)stream);

@@ -127,6 +127,8 @@ hipError_t launch_gemv_grouped(const GemvLaunch& a, const int32_t* offsets, cons
                                hipStream_t s);
 hipError_t launch_route(const RouteLaunch& a, hipStream_t s);
 hipError_t launch_grouped_gemm(const GemmLaunch& a, hipStream_t s);
+hipError_t launch_swiglu(const float* y_gu, int64_t P, int64_t I, uint16_t* h, hipStream_t s);
+hipError_t launch_combine(const float* y, const float* w, int64_t T, int k, int64_t out, float* yc, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, hipStream_t s);
 
 }  // namespace iqk

@@ -218,6 +218,23 @@ int iqk_moe_auto(const iqk_weights* w, const float* values, const int8_t* grid,
                  const void* x, int x_dtype, int x_slots, const int32_t* ids, int64_t T, int k,
                  void* workspace, size_t ws_bytes, float* y, int* path, void* stream);
 
+/* The layer steps either side of the projections for the prefill paths
+ * (the decode matvec has them as epilogues: iqk_moe_gemv_swiglu,
+ * iqk_moe_gemv_combine), with the same arithmetic (SwiGLU of the same
+ * gate/up sums gives the same bits; the combine agrees to float32
+ * rounding).  iqk_swiglu: y_gu device float32 [P, 2I] (per pair, gate
+ * columns [0, I) then up columns [I, 2I), as a gate/up projection writes
+ * them) -> h device bf16 [P, I], h = silu(g) * u, silu(g) = g / (1 +
+ * exp(-g)) in float32, one round-to-nearest-even cast.  I % 4 == 0
+ * (IQK_E_SHAPE); y_gu 16-byte and h 8-byte aligned.  iqk_combine: y device
+ * float32 [T, k, out], route_w device float32 [T, k] -> yc device float32
+ * [T, out], yc[t] = sum_j route_w[t, j] * y[t, j] (each product rounded,
+ * summed in slot order j = 0..k-1; a NaN in a slot makes that output NaN).
+ * out % 4 == 0 (IQK_E_SHAPE); y and yc 16-byte aligned. */
+int iqk_swiglu(const float* y_gu, int64_t P, int64_t I, uint16_t* h, void* stream);
+int iqk_combine(const float* y, const float* route_w, int64_t T, int k, int64_t out, float* yc,
+                void* stream);
+
 /* Routing gather ("Surface": sorting pairs by expert so that each expert's
  * weights are read once).  ids: device int32 [P] (P = T*k pair indices
  * t*k + j).  Writes device int32 counts[E], offsets[E+1] (exclusive prefix

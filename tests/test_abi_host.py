@@ -136,6 +136,13 @@ def test_validation_errors_before_any_launch():
     assert nb.value == 4 * 64 * 512 * 2 + 256 + 256 + 256
     assert L.iqk_moe_prefill(ctypes.byref(w), vp, None, fake, 1, fake, 8, 6, 0, fake, nb.value - 1, fake, s0) == q._E_SIZE
     assert L.iqk_moe_prefill(ctypes.byref(w), vp, None, fake, 1, fake, 0, 6, 0, fake, nb.value, fake, s0) == 0
+    # standalone glue: widths in fours, alignment
+    assert L.iqk_swiglu(fake, 4, 6, fake, s0) == q._E_SHAPE
+    assert L.iqk_swiglu(P(0x1008), 4, 8, fake, s0) == q._E_ARG
+    assert L.iqk_swiglu(fake, 0, 8, None, s0) == 0
+    assert L.iqk_combine(fake, fake, 2, 6, 10, fake, s0) == q._E_SHAPE
+    assert L.iqk_combine(fake, fake, 2, 0, 8, fake, s0) == q._E_ARG
+    assert L.iqk_combine(fake, fake, 0, 6, 8, fake, s0) == 0
     # fused prefill and grouped matvec: routing arrays plus an int64 [E + 1] work plan
     assert L.iqk_moe_prefill_fused_workspace(ctypes.byref(w), 8, 6, ctypes.byref(nb)) == 0
     assert nb.value == 256 + 256 + 256 + 256

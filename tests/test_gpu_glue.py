@@ -108,3 +108,58 @@ def test_swiglu_invalid_ids_give_nan_rows():
     assert np.all(np.isnan(h[0, 1])) and np.all(np.isnan(h[0, 2]))
     ref = oracle.swiglu(oracle.moe(fmt, s, E, 2 * I, n, x, ids, values))
     assert np.all(rel_err_per_vector(h[0, [0, 3]], ref[0, [0, 3]]) <= TOL_SWIGLU)
+
+
+# ---------------------------------------------------------------------------
+# standalone glue kernels (the prefill paths' layer steps)
+# ---------------------------------------------------------------------------
+
+def test_standalone_swiglu_matches_oracle_and_the_epilogue():
+    """iqk_swiglu on a gate/up output: oracle bar on random inputs (including
+    large |g| where exp overflows), and bit-identical to the decode epilogue
+    on the same projection"""
+    rng = np.random.default_rng(1000)
+    P, I = 37, 52
+    y = (rng.standard_normal((P, 2 * I)) * 4).astype(np.float32)
+    y[0, :4] = [0.0, -0.0, 95.0, -95.0]   # silu(0) = 0; exp(-g) overflow and underflow
+    announce("standalone swiglu")
+    h = q.swiglu(to_dev(y)).float().cpu().numpy()
+    ref = oracle.swiglu(y.astype(np.float64))
+    assert np.all(rel_err_per_vector(h, ref) <= TOL_SWIGLU)
+    # against the epilogue: the same gate/up sums through either route
+    fmt, n, I2, E, T, k = K, 2048, 64, 8, 3, 6
+    w, s = _weights(fmt, E, 2 * I2, n, 1001)
+    values = synth.values_table(1002)
+    ids, x = _inputs(1001, T, k, E, 1, n)
+    xd, idd = to_dev(x, torch.bfloat16), to_dev(ids)
+    h_epi = q.moe_gemv_swiglu(w, xd, idd, values)
+    h_two = q.swiglu(q.moe_gemv(w, xd, idd, values))
+    assert np.array_equal(h_epi.cpu().view(torch.int16).numpy(), h_two.cpu().view(torch.int16).numpy())
+
+
+def test_standalone_combine_matches_oracle_and_the_epilogue():
+    rng = np.random.default_rng(1010)
+    T, k, out = 9, 6, 40
+    y = rng.standard_normal((T, k, out)).astype(np.float32)
+    rw = rng.dirichlet(np.ones(k), size=T).astype(np.float32)
+    y[3, 2, 5] = np.nan
+    announce("standalone combine")
+    yc = q.combine(to_dev(y), to_dev(rw)).cpu().numpy()
+    ref = oracle.combine(y.astype(np.float64), rw)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(yc), nan) and nan.sum() == 1 and nan[3, 5]
+    scale = np.sum(np.abs(rw)[:, :, None] * np.abs(y), axis=1)
+    assert np.all(np.abs(yc[~nan] - ref[~nan]) <= 1e-6 * scale[~nan])
+    # against the epilogue: the same per-slot sums through either route
+    fmt, n, out2, E, T2 = KS, 2048, 48, 10, 4
+    w, s = _weights(fmt, E, out2, n, 1011)
+    values = synth.values_table(1012)
+    ids, x = _inputs(1011, T2, k, E, k, n)
+    rw2 = rng.dirichlet(np.ones(k), size=T2).astype(np.float32)
+    xd, idd, rwd = to_dev(x, torch.bfloat16), to_dev(ids), to_dev(rw2)
+    y_epi = q.moe_gemv_combine(w, xd, idd, rwd, values).cpu().numpy()
+    parts = q.moe_gemv(w, xd, idd, values, x_slots=k)
+    y_two = q.combine(parts, rwd).cpu().numpy()
+    pv = parts.cpu().numpy()
+    scale = np.sum(np.abs(rw2)[:, :, None] * np.abs(pv), axis=1)
+    assert np.all(np.abs(y_epi - y_two) <= 1e-6 * scale)

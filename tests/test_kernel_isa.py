@@ -46,7 +46,7 @@ def _kernels(asm: str):
     return bodies, meta
 
 
-@pytest.mark.parametrize("src", ["iqk_gemv.hip", "iqk_dequant.hip", "iqk_prefill.hip", "iqk_fused.hip"])
+@pytest.mark.parametrize("src", ["iqk_gemv.hip", "iqk_dequant.hip", "iqk_prefill.hip", "iqk_fused.hip", "iqk_glue.hip"])
 def test_no_scratch(src, tmp_path):
     bodies, meta = _kernels(_device_asm(src, tmp_path))
     assert meta, "no kernels found"
