@@ -710,9 +710,15 @@ hipError_t launch_inst(GemvParams p, int64_t T, hipStream_t s) {
         p.ubase = (int32_t)(upo / bpt);
         p.urem = (int32_t)(upo % bpt);
     } else {
-        // one large workgroup per CU over the whole call; more blocks only
-        // when a block would otherwise span more than max_x_rows pairs
-        nb = total < IQK_GEMV_TARGET_BLOCKS ? total : IQK_GEMV_TARGET_BLOCKS;
+        // one large workgroup per CU over the whole call -- or two smaller
+        // ones when each then holds at most 16 groups (at most 8 waves, so
+        // both stay resident on the CU): measured faster for a one-token
+        // launch, where two blocks' start-ups overlap the other's decode;
+        // more blocks only when a block would otherwise span more than
+        // max_x_rows pairs
+        int64_t target = IQK_GEMV_TARGET_BLOCKS;
+        if (total <= 2 * target * 16) target *= 2;
+        nb = total < target ? total : target;
         // a block of at most (span - 1) * upo + 1 units touches at most span outers
         const int64_t span_units = (max_x_rows<MODE>() - 1) * upo + 1;
         const int64_t nb_span = (total + span_units - 1) / span_units;
