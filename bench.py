@@ -447,20 +447,30 @@ GEMV_SOURCES = ("dequant_iqk_moe_amd/csrc/iqk_gemv.hip", "dequant_iqk_moe_amd/cs
 def measured_traffic():
     """HBM bytes per gate/up launch from the committed FETCH_SIZE/WRITE_SIZE
     summary, or None when the kernel sources changed since it was taken."""
-    import hashlib
     try:
         text = open(TRAFFIC_PROFILE).read()
     except OSError:
         return None
     fields = dict(line.split(": ", 1) for line in text.splitlines()
                   if line.startswith(("traffic_bytes_per_launch: ", "source_sha256: ")))
-    h = hashlib.sha256()
-    for rel in GEMV_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    if fields.get("source_sha256", "").strip() != h.hexdigest():
+    if fields.get("source_sha256", "").strip() != gemv_source_hash():
         return None
     return int(fields["traffic_bytes_per_launch"])
+
+
+def gemv_source_hash():
+    """sha256 over the matvec sources with comments and whitespace removed
+    (a comment edit does not change the kernel the counters measured)"""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for rel in GEMV_SOURCES:
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
 
 
 def pmc_launches(torch, q, synth, seed):

@@ -33,16 +33,24 @@
 // read and converted first (row loads issued before it would queue ahead of
 // it), the workgroup barrier waits only for LDS traffic, every wave then
 // requests its first two row groups at once and each later group two groups
-// ahead.  One large workgroup per CU (up to 16 waves)
-// amortizes the activation conversion over ~100 rows.  Rows of a workgroup
-// are contiguous, so the small per-row planes share cache lines.
+// ahead.  One large workgroup per CU (up to 16 waves) amortizes the
+// activation conversion over ~100 rows; a launch small enough for two
+// workgroups of at most 8 waves each per CU runs two, so one block's
+// start-up overlaps the other's decode.  Rows of a workgroup are
+// contiguous, so the small per-row planes share cache lines.
+//
+// The grouped matvec at the end of this file serves a few tokens per
+// expert: after the routing gather, one pass over each selected expert's
+// rows decodes every chunk once into int8 weight words and multiplies it
+// with all of the expert's tokens, whose activations each lane converts
+// into its own registers (a lane's chunk of k is the same for every row).
 #include "iqk_device.h"
 
 namespace iqk {
 namespace {
 
 #ifndef IQK_GEMV_TARGET_BLOCKS
-#define IQK_GEMV_TARGET_BLOCKS 256  // workgroups per launch (one per CU)
+#define IQK_GEMV_TARGET_BLOCKS 256  // workgroups per launch (one per CU; two for small launches)
 #endif
 #ifndef IQK_GEMV_MIN_GROUPS
 #define IQK_GEMV_MIN_GROUPS 2       // reduction groups per wave when the block has >= 8
