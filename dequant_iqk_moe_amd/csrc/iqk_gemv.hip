@@ -214,6 +214,13 @@ struct XLds {
     int32_t bsum[N / 32];
 };
 
+// 16-byte slot of block i (0..3) of 64-value chunk c in an XLds plane.  The
+// decode reads block i of chunk c = lane in one ds_read_b128 per wave;
+// rotating the four blocks of a chunk by c / 4 puts the eight lanes served
+// in one LDS cycle (chunks c and c + 4 would otherwise share banks) on
+// distinct banks.
+__device__ __forceinline__ int xslot(int c, int i) { return 4 * c + ((i + (c >> 2)) & 3); }
+
 // Raw activation words of one 16-value block (bf16: 8 words, f32: 16).
 template <int XDT>
 struct XRaw {
@@ -281,8 +288,9 @@ __device__ __forceinline__ void prep_block(const XRaw<XDT>& raw, XLds<N>& L, int
         wl[j] = (uint32_t)(lo[i0] & 0xFF) | ((uint32_t)(lo[i0 + st] & 0xFF) << 8) |
                 ((uint32_t)(lo[i0 + 2 * st] & 0xFF) << 16) | ((uint32_t)(lo[i0 + 3 * st] & 0xFF) << 24);
     }
-    *(uint4*)&L.hi[4 * b] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-    *(uint4*)&L.lo[4 * b] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+    const int slot = xslot(b >> 2, b & 3);
+    *(uint4*)&L.hi[4 * slot] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+    *(uint4*)&L.lo[4 * slot] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
     if ((b & 3) == 0) L.scale[b >> 2] = __builtin_ldexpf(1.0f, emax - 13);
     if constexpr (FMT == IQK_IQ1_S_R4) {
         int sum = 0;
@@ -595,8 +603,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
     auto load_x = [&](int xi) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint4 a = *(const uint4*)&X[xi].hi[16 * c + 4 * i];
-            const uint4 b = *(const uint4*)&X[xi].lo[16 * c + 4 * i];
+            const uint4 a = *(const uint4*)&X[xi].hi[4 * xslot(c, i)];
+            const uint4 b = *(const uint4*)&X[xi].lo[4 * xslot(c, i)];
             xh[4 * i] = a.x; xh[4 * i + 1] = a.y; xh[4 * i + 2] = a.z; xh[4 * i + 3] = a.w;
             xl[4 * i] = b.x; xl[4 * i + 1] = b.y; xl[4 * i + 2] = b.z; xl[4 * i + 3] = b.w;
         }
