@@ -51,7 +51,9 @@ def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
+    # 6000 steps (~0.1 s): the GPU raises its clocks over ~10-20 ms of load
+    # after idling, so the timed steps start at the steady clock
+    ap.add_argument("--warmup", type=int, default=6000)
     ap.add_argument("--cells", choices=["none", "all", "prefill"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=2)
@@ -99,8 +101,24 @@ class Pools:
         return len(np.unique(ids)) * self.out * self.row_bytes
 
 
-def timed_graph(torch, fn, S, reps, warm_reps):
-    """Capture S calls of fn(i) in one graph; replay; return ms per call."""
+# Secondary cells run after host-side work (validation, oracle rows) that
+# leaves the GPU idle and its clocks lowered; each is run for this long
+# (untimed) before it is timed.  Measured: a 0.5 ms fused prefill call takes
+# ~20 % longer, and a T=1 decode launch ~5 % longer, in the first ~10 ms
+# after an idle second.
+CLOCK_RAMP_S = 0.05
+
+
+def ramp_clocks(torch, run):
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < CLOCK_RAMP_S:
+        run()
+        torch.cuda.synchronize()
+
+
+def timed_graph(torch, fn, S, reps, warm_reps, ramp=True):
+    """Capture S calls of fn(i) in one graph; replay; return ms per call.
+    ramp=False keeps the warm-up to exactly warm_reps replays."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -115,6 +133,8 @@ def timed_graph(torch, fn, S, reps, warm_reps):
     for _ in range(warm_reps):
         g.replay()
     torch.cuda.synchronize()
+    if ramp:
+        ramp_clocks(torch, g.replay)
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -130,6 +150,7 @@ def timed_eager(torch, fn, reps, warm):
     for i in range(warm):
         fn(i)
     torch.cuda.synchronize()
+    ramp_clocks(torch, lambda: fn(0))
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -330,8 +351,13 @@ def prefill_cells(ctx, fmt, seed):
         wbytes = E * rows * q.row_bytes(fmt, n)
         dbytes = E * rows * n * 2
         dv = dense.view(E * rows, n)
-        prod_ms = timed_eager(torch, lambda i: q.dequant(w, ctx.values, grid, torch.bfloat16, out=dv), 10, 2)
-        floor_ms = timed_eager(torch, lambda i: q.floor_dequant(w, torch.bfloat16, out=dv), 10, 2)
+        # producer and floor arms alternate (three rounds each, medians)
+        arms = {"prod": [], "floor": []}
+        for _ in range(3):
+            arms["prod"].append(timed_eager(torch, lambda i: q.dequant(w, ctx.values, grid, torch.bfloat16, out=dv),
+                                            10, 2))
+            arms["floor"].append(timed_eager(torch, lambda i: q.floor_dequant(w, torch.bfloat16, out=dv), 10, 2))
+        prod_ms, floor_ms = float(np.median(arms["prod"])), float(np.median(arms["floor"]))
         q.dequant(w, ctx.values, grid, torch.bfloat16, out=dv)  # the floor left raw words in the dense copy
         pbytes = wbytes + dbytes
         pg = pbytes / (prod_ms * 1e-3) / 1e9
@@ -623,7 +649,7 @@ def main():
         q.moe_gemv(gate_up.w[p], x, ids_dev[i], values, y=y1)
         q.moe_gemv(down.w[p], h, ids_dev[i], values, x_slots=K, y=y2)
 
-    ms_step = timed_graph(torch, step, S, reps, warm)
+    ms_step = timed_graph(torch, step, S, reps, warm, ramp=False)
     bytes_steps = [gate_up.bytes_for(a) + down.bytes_for(a) + x.numel() * 2 + y1.numel() * 4 + h.numel() * 2
                    + y2.numel() * 4 for a in ids_host]
     bytes_per_step = float(np.mean(bytes_steps))
