@@ -653,12 +653,12 @@ int iqk_moe_auto(const iqk_weights* w, const float* values, const int8_t* grid, 
     if (rc) return rc;
     if (T < 0 || k <= 0) return fail(IQK_E_ARG, "T must be >= 0 and k > 0");
     // measured crossover on the routed geometry (top-6 of 256 experts): with
-    // in = 4096 the per-pair matvec up to 16 tokens (3/8 pair per expert),
+    // in = 4096 the per-pair matvec up to 32 tokens (3/4 pair per expert),
     // the grouped matvec up to 64 (3/2), the fused prefill beyond; with a
     // narrower input the per-pair matvec up to 32 tokens (3/4), then the
     // fused prefill
     const double per_expert = (double)(T * k) / (double)w->experts;
-    const double lim_pair = w->in >= 4096 ? 0.375 : 0.75;
+    const double lim_pair = 0.75;
     const double lim_grouped = w->in >= 4096 ? 1.5 : 0.75;
     uint32_t lo = 0, hi = 0;
     float sc = 1.f;

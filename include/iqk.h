@@ -204,10 +204,9 @@ int iqk_moe_auto_workspace(const iqk_weights* w, int64_t T, int k, size_t* bytes
 /* The routed projection y[T, k, out] with the path chosen by the number of
  * token-expert pairs ("Surface": few pairs take the fused decode, many the
  * prefill), with the crossover measured on the routed geometry (top-6 of
- * 256 experts): for in = 4096, pairs per expert T*k/E <= 3/8 ->
- * iqk_moe_gemv, <= 3/2 -> iqk_moe_gemv_grouped, above ->
- * iqk_moe_prefill_fused; for narrower inputs <= 3/4 -> iqk_moe_gemv, above
- * -> iqk_moe_prefill_fused.  A float32 activation never takes the prefill
+ * 256 experts): pairs per expert T*k/E <= 3/4 -> iqk_moe_gemv; above
+ * that, for in = 4096, <= 3/2 -> iqk_moe_gemv_grouped and above ->
+ * iqk_moe_prefill_fused; for narrower inputs iqk_moe_prefill_fused.  A float32 activation never takes the prefill
  * (it needs bf16); a value table that is not int8-exact takes the prefill
  * when x is bf16 (else IQK_E_TABLE).  *path (if non-null) receives 0, 1 or
  * 2 for the path taken.  Arguments and errors are those of the chosen call;
