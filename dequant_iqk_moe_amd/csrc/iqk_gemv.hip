@@ -264,8 +264,10 @@ __device__ __forceinline__ void prep_block(const XRaw<XDT>& raw, XLds<N>& L, int
     uint32_t amax = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax = max(amax, __float_as_uint(v[i]) & 0x7FFFFFFFu);
-    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
-    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+    // the chunk's four blocks sit in one quad of lanes, all active together
+    // (DPP within the quad, no LDS round trip)
+    amax = max(amax, dpp_xor1(amax));
+    amax = max(amax, dpp_xor2(amax));
     int emax = (int)(amax >> 23) - 127;
     emax = emax < -100 ? -100 : emax;
     const float s = __builtin_ldexpf(1.0f, 13 - emax);
@@ -296,7 +298,7 @@ __device__ __forceinline__ void prep_block(const XRaw<XDT>& raw, XLds<N>& L, int
         int sum = 0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sum += q[i];
-        sum += __shfl_xor(sum, 1);
+        sum += (int)dpp_xor1((uint32_t)sum);
         if ((b & 1) == 0) L.bsum[b >> 1] = sum;
     }
 }
@@ -650,7 +652,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
         } else if constexpr (MODE == kSwiGLU) {
             // gate row q < RPG/2 and its up row q + RPG/2 sit 32 lanes apart
             // (16 when a row spans 32 lanes)
-            const uint32_t up = (uint32_t)__shfl_xor((int)sum, G::LPR == 32 ? 16 : 32);
+            // (a lane swap on the VALU: the second half of the pair holds, in
+            // the gate row's lanes, the other row group's value)
+            uint32_t up;
+            if constexpr (G::LPR == 32) up = __builtin_amdgcn_permlane16_swap(sum, sum, false, false)[1];
+            else up = __builtin_amdgcn_permlane32_swap(sum, sum, false, false)[1];
             const float g = __uint_as_float(sum);
             const float hv = g / (1.0f + expf(-g)) * __uint_as_float(up);
             const int r = rem * kHalf + q;  // h index inside the pair
