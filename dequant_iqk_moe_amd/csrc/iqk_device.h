@@ -1,5 +1,6 @@
 // iqk_device.h -- device-side access to the canonical per-row streams,
-// shared by the decode matvec and the fused prefill.
+// shared by the decode matvec and the fused prefill (and the SwiGLU
+// arithmetic shared by the matvec epilogue and the standalone glue kernel).
 //
 // "mlx-iqk" package description, "Format": per-row planes (qs, scl, sch,
 // sex, dv for the 2-bit members; qs, qh, dv for IQ1_S_R4), here stored
@@ -11,6 +12,16 @@
 #include "iqk_internal.h"
 
 namespace iqk {
+
+// silu(g) * u = g / (1 + exp(-g)) * u in float32, with the hardware
+// exponential (v_exp_f32 of -g log2 e) and reciprocal (v_rcp_f32): about an
+// ulp each, far below the bf16 rounding the SwiGLU output gets.  One
+// definition for the matvec epilogue and the standalone kernel, so the two
+// agree bit for bit.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
 
 __device__ __forceinline__ float half_to_float(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);

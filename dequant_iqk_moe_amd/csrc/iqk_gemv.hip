@@ -658,7 +658,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
             if constexpr (G::LPR == 32) up = __builtin_amdgcn_permlane16_swap(sum, sum, false, false)[1];
             else up = __builtin_amdgcn_permlane32_swap(sum, sum, false, false)[1];
             const float g = __uint_as_float(sum);
-            const float hv = g / (1.0f + expf(-g)) * __uint_as_float(up);
+            const float hv = silu_mul(g, __uint_as_float(up));
             const int r = rem * kHalf + q;  // h index inside the pair
             const Rsrc hres = make_rsrc(p.h + (int64_t)pair * half_out, (uint32_t)half_out * 2u);
             __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16(hv), hres,

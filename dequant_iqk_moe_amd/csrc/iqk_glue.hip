@@ -6,11 +6,11 @@
 // switch-linear call y[T, k, out] = proj(x, indices); a SwiGLU expert feeds
 // silu(gate) * up of its gate/up projection to down, and the layer output is
 // the router-weighted sum of the k slots.  The arithmetic is the decode
-// epilogues': h = g / (1 + exp(-g)) * u in float32, one round-to-nearest-even
-// cast to bf16; y[t] = sum_j (w[t, j] * y[t, j]) with each product rounded
+// epilogues': h = g / (1 + exp(-g)) * u in float32 (silu_mul), one
+// round-to-nearest-even cast to bf16; y[t] = sum_j (w[t, j] * y[t, j]) with each product rounded
 // once and the sum taken in slot order.  Both are HBM-bound elementwise
 // passes (16-byte loads, grid-stride).
-#include "iqk_internal.h"
+#include "iqk_device.h"
 
 namespace iqk {
 namespace {
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kGlueThreads) void swiglu_kernel(const float* __res
         const float uv[4] = {u.x, u.y, u.z, u.w};
         uint32_t o[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = glue_bf16(gv[j] / (1.0f + expf(-gv[j])) * uv[j]);
+        for (int j = 0; j < 4; ++j) o[j] = glue_bf16(silu_mul(gv[j], uv[j]));
         *(uint2*)(h + p * I + c) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
     }
 }

@@ -156,8 +156,9 @@ int iqk_moe_gemv(const iqk_weights* w, const float* values, const int8_t* grid,
  * "Surface" used the way a SwiGLU expert uses it): the same matvec over a
  * gate/up tensor whose rows [0, I) are gate and [I, 2I) up (out = 2I, even,
  * else IQK_E_SHAPE), written as h[t, j, i] = silu(g) * u with
- * g = gate_i . x, u = up_i . x, silu(g) = g / (1 + exp(-g)) in float32, and
- * h stored as bf16 (round to nearest even): device uint16 [T, k, I].  This is
+ * g = gate_i . x, u = up_i . x, silu(g) = g / (1 + exp(-g)) in float32 (the
+ * hardware exponential and reciprocal, about an ulp each), and h stored as
+ * bf16 (round to nearest even): device uint16 [T, k, I].  This is
  * the down projection's per-pair input.  Invalid ids give NaN rows.
  * Arguments and limits otherwise as iqk_moe_gemv. */
 int iqk_moe_gemv_swiglu(const iqk_weights* w, const float* values, const int8_t* grid,
@@ -223,8 +224,8 @@ int iqk_moe_auto(const iqk_weights* w, const float* values, const int8_t* grid,
  * gate/up sums gives the same bits; the combine agrees to float32
  * rounding).  iqk_swiglu: y_gu device float32 [P, 2I] (per pair, gate
  * columns [0, I) then up columns [I, 2I), as a gate/up projection writes
- * them) -> h device bf16 [P, I], h = silu(g) * u, silu(g) = g / (1 +
- * exp(-g)) in float32, one round-to-nearest-even cast.  I % 4 == 0
+ * them) -> h device bf16 [P, I], h = silu(g) * u as in
+ * iqk_moe_gemv_swiglu, one round-to-nearest-even cast.  I % 4 == 0
  * (IQK_E_SHAPE); y_gu 16-byte and h 8-byte aligned.  iqk_combine: y device
  * float32 [T, k, out], route_w device float32 [T, k] -> yc device float32
  * [T, out], yc[t] = sum_j route_w[t, j] * y[t, j] (each product rounded,
