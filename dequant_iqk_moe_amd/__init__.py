@@ -68,7 +68,7 @@ def library_path() -> str:
 
 def _load():
     if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is not built; run `python -m dequant_iqk_moe_amd.build`")
+        raise ImportError(f"{_LIB_PATH} is not built; run `python dequant_iqk_moe_amd/build.py`")
     L = ctypes.CDLL(_LIB_PATH)
     p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
     W = ctypes.POINTER(_Weights)

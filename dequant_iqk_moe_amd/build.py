@@ -3,7 +3,7 @@
 Every ``.hip`` file is compiled for ``--offload-arch=gfx950`` with packed-FP32
 instructions disabled; the dequantization kernels additionally forbid FMA
 contraction so each float32 step of the reconstruction rounds on its own.
-Run ``python -m dequant_iqk_moe_amd.build`` (or ``__graft_entry__.build()``).
+Run ``python dequant_iqk_moe_amd/build.py`` (or ``__graft_entry__.build()``).
 """
 from __future__ import annotations
 
