@@ -221,6 +221,12 @@ struct XLds {
 // distinct banks.
 __device__ __forceinline__ int xslot(int c, int i) { return 4 * c + ((i + (c >> 2)) & 3); }
 
+// Two 16-bit lanes added without a carry between them (v_pk_add_u16).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t add_u16x2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a) + __builtin_bit_cast(u16x2, b));
+}
+
 // Raw activation words of one 16-value block (bf16: 8 words, f32: 16).
 template <int XDT>
 struct XRaw {
@@ -261,23 +267,24 @@ __device__ __forceinline__ void prep_block(const XRaw<XDT>& raw, XLds<N>& L, int
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(raw.w[i]);
     }
-    uint32_t amax = 0;
+    float am = 0.f;  // (v_max3_f32 with |.| source modifiers)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = max(amax, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+    for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[i]));
     // the chunk's four blocks sit in one quad of lanes, all active together
-    // (DPP within the quad, no LDS round trip)
+    // (DPP within the quad, no LDS round trip); non-negative floats order as
+    // their bit patterns
+    uint32_t amax = __float_as_uint(am);
     amax = max(amax, dpp_xor1(amax));
     amax = max(amax, dpp_xor2(amax));
     int emax = (int)(amax >> 23) - 127;
     emax = emax < -100 ? -100 : emax;
     const float s = __builtin_ldexpf(1.0f, 13 - emax);
-    int hi[16], lo[16], q[16];
+    int q[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        q[i] = (int)__builtin_rintf(v[i] * s);  // |q| <= 2^14
-        hi[i] = (q[i] + 128) >> 8;
-        lo[i] = q[i] - (hi[i] << 8);
-    }
+    for (int i = 0; i < 16; ++i) q[i] = (int)__builtin_rintf(v[i] * s);  // |q| <= 2^14
+    // q = 256 hi + lo with lo in [-128, 127]: lo is q's low byte and hi the
+    // second byte of q + 128 (16-bit), so each plane word is byte gathers
+    // (v_perm_b32) of q packed two to a word, plus one packed 16-bit add.
     uint32_t wh[4], wl[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -285,10 +292,10 @@ __device__ __forceinline__ void prep_block(const XRaw<XDT>& raw, XLds<N>& L, int
         // IQ1_S_R4: natural order
         const int i0 = FMT == IQK_IQ1_S_R4 ? 4 * j : j;
         const int st = FMT == IQK_IQ1_S_R4 ? 1 : 4;
-        wh[j] = (uint32_t)(hi[i0] & 0xFF) | ((uint32_t)(hi[i0 + st] & 0xFF) << 8) |
-                ((uint32_t)(hi[i0 + 2 * st] & 0xFF) << 16) | ((uint32_t)(hi[i0 + 3 * st] & 0xFF) << 24);
-        wl[j] = (uint32_t)(lo[i0] & 0xFF) | ((uint32_t)(lo[i0 + st] & 0xFF) << 8) |
-                ((uint32_t)(lo[i0 + 2 * st] & 0xFF) << 16) | ((uint32_t)(lo[i0 + 3 * st] & 0xFF) << 24);
+        const uint32_t w01 = __builtin_amdgcn_perm((uint32_t)q[i0 + st], (uint32_t)q[i0], 0x05040100u);
+        const uint32_t w23 = __builtin_amdgcn_perm((uint32_t)q[i0 + 3 * st], (uint32_t)q[i0 + 2 * st], 0x05040100u);
+        wl[j] = __builtin_amdgcn_perm(w23, w01, 0x06040200u);
+        wh[j] = __builtin_amdgcn_perm(add_u16x2(w23, 0x00800080u), add_u16x2(w01, 0x00800080u), 0x07050301u);
     }
     const int slot = xslot(b >> 2, b & 3);
     *(uint4*)&L.hi[4 * slot] = make_uint4(wh[0], wh[1], wh[2], wh[3]);

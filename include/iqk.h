@@ -136,7 +136,8 @@ int iqk_dequant(const iqk_weights* w, int64_t row0, int64_t nrows, const float* 
 /* Fused decode matvec ("Surface": few token-expert pairs).
  * y[t, j, o] = sum_k W_{ids[t,j]}[o, k] * x[t, s, k] with s = 0 if
  * x_slots == 1 (shared input, gate/up) or s = j if x_slots == k (per-pair
- * input, down).  x: device [T, x_slots, in] of x_dtype IQK_F32 or IQK_BF16.
+ * input, down).  x: device [T, x_slots, in] of x_dtype IQK_F32 or IQK_BF16,
+ * finite (a NaN or infinite activation gives an unspecified result).
  * ids: device int32 [T, k]; an id outside [0, experts) gives a NaN output
  * row.  y: device float32 [T, k, out].
  * Widths: in must be 512, 2048 or 4096 (IQK_E_WIDTH otherwise): a kernel
