@@ -279,9 +279,13 @@ __device__ __forceinline__ void prep_block(const XRaw<XDT>& raw, XLds<N>& L, int
     int emax = (int)(amax >> 23) - 127;
     emax = emax < -100 ? -100 : emax;
     const float s = __builtin_ldexpf(1.0f, 13 - emax);
-    int q[16];
+    // q = rint(v s), |q| <= 2^14, as one v_fma_f32: v s + 1.5 2^23 lands in
+    // [2^23, 2^24), where float32 steps are 1, and rounds once to the
+    // nearest integer, ties to even as rint (the added constant is even);
+    // the word is then 0x4B400000 + q, whose low 16 bits are q's.
+    uint32_t q[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) q[i] = (int)__builtin_rintf(v[i] * s);  // |q| <= 2^14
+    for (int i = 0; i < 16; ++i) q[i] = __float_as_uint(__builtin_fmaf(v[i], s, 12582912.0f));
     // q = 256 hi + lo with lo in [-128, 127]: lo is q's low byte and hi the
     // second byte of q + 128 (16-bit), so each plane word is byte gathers
     // (v_perm_b32) of q packed two to a word, plus one packed 16-bit add.
@@ -292,8 +296,8 @@ __device__ __forceinline__ void prep_block(const XRaw<XDT>& raw, XLds<N>& L, int
         // IQ1_S_R4: natural order
         const int i0 = FMT == IQK_IQ1_S_R4 ? 4 * j : j;
         const int st = FMT == IQK_IQ1_S_R4 ? 1 : 4;
-        const uint32_t w01 = __builtin_amdgcn_perm((uint32_t)q[i0 + st], (uint32_t)q[i0], 0x05040100u);
-        const uint32_t w23 = __builtin_amdgcn_perm((uint32_t)q[i0 + 3 * st], (uint32_t)q[i0 + 2 * st], 0x05040100u);
+        const uint32_t w01 = __builtin_amdgcn_perm(q[i0 + st], q[i0], 0x05040100u);
+        const uint32_t w23 = __builtin_amdgcn_perm(q[i0 + 3 * st], q[i0 + 2 * st], 0x05040100u);
         wl[j] = __builtin_amdgcn_perm(w23, w01, 0x06040200u);
         wh[j] = __builtin_amdgcn_perm(add_u16x2(w23, 0x00800080u), add_u16x2(w01, 0x00800080u), 0x07050301u);
     }
@@ -302,10 +306,10 @@ __device__ __forceinline__ void prep_block(const XRaw<XDT>& raw, XLds<N>& L, int
     *(uint4*)&L.lo[4 * slot] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
     if ((b & 3) == 0) L.scale[b >> 2] = __builtin_ldexpf(1.0f, emax - 13);
     if constexpr (FMT == IQK_IQ1_S_R4) {
-        int sum = 0;
+        uint32_t sum = 0u - 16u * 0x4B400000u;  // (wrapping) sum of the q
 #pragma unroll
         for (int i = 0; i < 16; ++i) sum += q[i];
-        sum += (int)dpp_xor1((uint32_t)sum);
+        sum += dpp_xor1(sum);
         if ((b & 1) == 0) L.bsum[b >> 1] = sum;
     }
 }
