@@ -381,7 +381,7 @@ __device__ __forceinline__ float row_dot(const RowData& r, int c, const uint32_t
             ah += __mul24(h[i], si);
             al += __mul24(l[i], si);
         }
-        return (float)ah * 256.0f + (float)al;
+        return (float)(ah * 256 + al);  // exact: |.| < 2^31, one rounding as before
     } else if constexpr (FMT == IQK_IQ2_KS) {
         const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
         const int sh = 2 * (c & 3);
@@ -399,7 +399,7 @@ __device__ __forceinline__ float row_dot(const RowData& r, int c, const uint32_t
             ah += __mul24(h, si);
             al += __mul24(l, si);
         }
-        return (float)ah * 256.0f + (float)al;
+        return (float)(ah * 256 + al);  // exact: |.| < 2^31, one rounding as before
     } else {
         float part = 0.f;
 #pragma unroll
@@ -418,7 +418,7 @@ __device__ __forceinline__ float row_dot(const RowData& r, int c, const uint32_t
                 al = __builtin_amdgcn_sdot4((int)gv.y, (int)xl[2 * g + 1], al, false);
             }
             const float shift = (h16 >> 15) ? -0.125f : 0.125f;
-            const float tb = (float)ah * 256.0f + (float)al + shift * (float)bsum[b];
+            const float tb = (float)(ah * 256 + al) + shift * (float)bsum[b];
             part += tb * (float)(2 * ((h16 >> 12) & 7u) + 1);
         }
         return part;
