@@ -867,43 +867,45 @@ __device__ __forceinline__ void lane_block(const void* xrow, int c, int blk, flo
 // conversion; the second pass reads them again from the cache)
 template <int FMT, int XDT>
 __device__ __forceinline__ void lane_x(const void* xrow, int c, float tab_scale, XLane& o) {
-    uint32_t amax = 0;
+    float am = 0.f;
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
         float v[16];
         lane_block<XDT>(xrow, c, blk, v);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) amax = max(amax, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+        for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[i]));
     }
+    const uint32_t amax = __float_as_uint(am);
     int emax = (int)(amax >> 23) - 127;
     emax = emax < -100 ? -100 : emax;
     const float sc = __builtin_ldexpf(1.0f, 13 - emax);
-    int32_t bs[2] = {0, 0};
+    // the per-pair matvec's conversion (prep_block): q = rint(v sc) through
+    // one fma against 1.5 2^23, planes as byte gathers of q
+    uint32_t bs[2] = {0u - 32u * 0x4B400000u, 0u - 32u * 0x4B400000u};
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
         float v[16];
         lane_block<XDT>(xrow, c, blk, v);
-        int hi[16], lo[16];
+        uint32_t q[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int q = (int)__builtin_rintf(v[i] * sc);  // |q| <= 2^14
-            hi[i] = (q + 128) >> 8;
-            lo[i] = q - (hi[i] << 8);
-            bs[blk >> 1] += q;
+            q[i] = __float_as_uint(__builtin_fmaf(v[i], sc, 12582912.0f));  // 0x4B400000 + q, |q| <= 2^14
+            bs[blk >> 1] += q[i];
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int i0 = FMT == IQK_IQ1_S_R4 ? 4 * j : j;
             const int st = FMT == IQK_IQ1_S_R4 ? 1 : 4;
-            o.hi[4 * blk + j] = (uint32_t)(hi[i0] & 0xFF) | ((uint32_t)(hi[i0 + st] & 0xFF) << 8) |
-                                ((uint32_t)(hi[i0 + 2 * st] & 0xFF) << 16) | ((uint32_t)(hi[i0 + 3 * st] & 0xFF) << 24);
-            o.lo[4 * blk + j] = (uint32_t)(lo[i0] & 0xFF) | ((uint32_t)(lo[i0 + st] & 0xFF) << 8) |
-                                ((uint32_t)(lo[i0 + 2 * st] & 0xFF) << 16) | ((uint32_t)(lo[i0 + 3 * st] & 0xFF) << 24);
+            const uint32_t w01 = __builtin_amdgcn_perm(q[i0 + st], q[i0], 0x05040100u);
+            const uint32_t w23 = __builtin_amdgcn_perm(q[i0 + 3 * st], q[i0 + 2 * st], 0x05040100u);
+            o.lo[4 * blk + j] = __builtin_amdgcn_perm(w23, w01, 0x06040200u);
+            o.hi[4 * blk + j] =
+                __builtin_amdgcn_perm(add_u16x2(w23, 0x00800080u), add_u16x2(w01, 0x00800080u), 0x07050301u);
         }
     }
     o.scale = __builtin_ldexpf(1.0f, emax - 13) * tab_scale;
-    o.bsum[0] = bs[0];
-    o.bsum[1] = bs[1];
+    o.bsum[0] = (int32_t)bs[0];
+    o.bsum[1] = (int32_t)bs[1];
 }
 
 // One lane's decoded 64-weight chunk of one row: int8 weight words w[i]
