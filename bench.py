@@ -590,7 +590,7 @@ def main():
     args = _parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; multi-GPU runs are not provided "
+        print(json.dumps({"error": "bench.py runs on exactly one GPU; multi-GPU runs are not provided "
                                    "(the expert-parallel sharding is described, not built)"}))
         sys.exit(2)
 

@@ -26,8 +26,12 @@ def _ensure_built():
     """Build the HIP library in-tree only when nothing is built yet."""
     lib = os.path.join(ROOT, "dequant_iqk_moe_amd", "libiqk.so")
     if not os.path.exists(lib):
-        from dequant_iqk_moe_amd import build as _b
-        _b.build()
+        # build.py by path: importing the package itself needs the library
+        import importlib.util
+        spec = importlib.util.spec_from_file_location("_iqk_build", os.path.join(ROOT, "dequant_iqk_moe_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
 
 
 _ensure_built()
