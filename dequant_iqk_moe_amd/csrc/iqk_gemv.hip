@@ -412,9 +412,10 @@ __device__ __forceinline__ float row_dot(const RowData& r, int c, const uint32_t
                 const int g = 4 * b + j;
                 const uint32_t idx = ((qsw >> (8 * j)) & 0xFFu) | (((h16 >> (3 * j)) & 7u) << 8);
                 const uint2 gv = grid_s[idx];
-                ah = __builtin_amdgcn_sdot4((int)gv.x, (int)xh[2 * g], ah, false);
+                // (the chain's first dot starts from an inline zero: no v_mov)
+                ah = j == 0 ? dot4_first(gv.x, xh[2 * g]) : __builtin_amdgcn_sdot4((int)gv.x, (int)xh[2 * g], ah, false);
                 ah = __builtin_amdgcn_sdot4((int)gv.y, (int)xh[2 * g + 1], ah, false);
-                al = __builtin_amdgcn_sdot4((int)gv.x, (int)xl[2 * g], al, false);
+                al = j == 0 ? dot4_first(gv.x, xl[2 * g]) : __builtin_amdgcn_sdot4((int)gv.x, (int)xl[2 * g], al, false);
                 al = __builtin_amdgcn_sdot4((int)gv.y, (int)xl[2 * g + 1], al, false);
             }
             const float shift = (h16 >> 15) ? -0.125f : 0.125f;
