@@ -91,11 +91,12 @@ def test_grouped_skewed_routing(fmt):
     assert np.all(rel_err_per_vector(y, ref) <= TOL_GEMV)
 
 
-@pytest.mark.parametrize("T,expect", [(2, "gemv"), (8, "grouped_gemv"), (20, "fused_prefill")])
+@pytest.mark.parametrize("T,expect", [(2, "gemv"), (6, "gemv"), (7, "grouped_gemv"), (8, "grouped_gemv"),
+                                      (12, "grouped_gemv"), (13, "fused_prefill"), (20, "fused_prefill")])
 def test_auto_dispatch_by_pairs_per_expert(T, expect):
-    """in = 4096: pairs per expert 0.25 / 1 / 2.5 pick the per-pair matvec,
-    the grouped matvec and the fused prefill; each result meets its path's
-    bar"""
+    """in = 4096, 16 experts, 2 slots: pairs per expert T/8 up to 3/4 (T = 6)
+    pick the per-pair matvec, up to 3/2 (T = 12) the grouped matvec, beyond
+    the fused prefill; each result meets its path's bar"""
     fmt, n, out, E, k = K, 4096, 64, 16, 2
     seed = 1600 + T
     w, s = _weights(fmt, E, out, n, seed)
