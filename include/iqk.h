@@ -146,10 +146,10 @@ int iqk_dequant(const iqk_weights* w, int64_t row0, int64_t nrows, const float* 
  * tables qualify), else IQK_E_TABLE.  IQ1_S_R4: grid values must lie in
  * [-8, 7] (the ternary grid does; the matvec holds each grid entry as eight
  * signed 4-bit values), else the result is unspecified.  Accuracy: the
- * activation is held per 64-value block as 15-bit fixed point (relative
- * error about 2^-14 of the block maximum); weights and sums are exact
- * integers up to one float32 rounding per row; ||y - y_exact|| /
- * ||y_exact|| <= 1e-3.
+ * activation is held per
+ * 64-value block as 15-bit fixed point (relative error about 2^-14 of the
+ * block maximum); weights and sums are exact integers up to one float32
+ * rounding per row; ||y - y_exact|| / ||y_exact|| <= 1e-3.
  * Limits: T * k <= 65535 * 64, out * iqk_row_bytes(fmt, in) < 2^31,
  * T * k * ceil(out / 4) < 2^31 (IQK_E_ARG otherwise). */
 int iqk_moe_gemv(const iqk_weights* w, const float* values, const int8_t* grid,
