@@ -143,10 +143,7 @@ int iqk_dequant(const iqk_weights* w, int64_t row0, int64_t nrows, const float* 
  * Widths: in must be 512, 2048 or 4096 (IQK_E_WIDTH otherwise): a kernel
  * instance makes exactly one pass over k.  The values table (host float[8])
  * must be m_i * 2^e with integer |m_i| <= 127 for one common e (integer
- * tables qualify), else IQK_E_TABLE.  IQ1_S_R4: grid values must lie in
- * [-8, 7] (the ternary grid does; the matvec holds each grid entry as eight
- * signed 4-bit values), else the result is unspecified.  Accuracy: the
- * activation is held per
+ * tables qualify), else IQK_E_TABLE.  Accuracy: the activation is held per
  * 64-value block as 15-bit fixed point (relative error about 2^-14 of the
  * block maximum); weights and sums are exact integers up to one float32
  * rounding per row; ||y - y_exact|| / ||y_exact|| <= 1e-3.
