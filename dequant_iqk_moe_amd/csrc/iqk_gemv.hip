@@ -24,12 +24,9 @@
 //     against the hi and lo planes accumulates exact int32 per sub-block,
 //     v_mad_i32_i24 applies the signed scale index.  The fixed-point x is
 //     pre-permuted in LDS to match the spread order, so no weight moves;
-//   * IQ1_S_R4: the 2048-entry ternary grid is staged in LDS as one word of
-//     eight signed nibbles per entry (8 KiB), and the fixed-point activation
-//     as four planes of signed base-16 digits instead of the two int8
-//     planes; each 8-weight group is one ds_read_b32 and four
-//     v_dot8_i32_i4, one per digit plane; the +-1/8 shift is applied
-//     through the block sum of x;
+//   * IQ1_S_R4: the 2048 x 8 int8 grid is staged in LDS (16 KiB); each
+//     8-weight group is one ds_read_b64 and four v_dot4_i32_i8, the +-1/8
+//     shift is applied through the block sum of x;
 //   * per-lane partials of 4 rows are reduced with v_permlane32_swap,
 //     v_permlane16_swap and DPP (10 instructions per 4 rows).
 // Latency: a decode launch is a few microseconds long.  The activation is
@@ -293,41 +290,16 @@ __device__ __forceinline__ void prep_block(const XRaw<XDT>& raw, XLds<N>& L, int
     // second byte of q + 128 (16-bit), so each plane word is byte gathers
     // (v_perm_b32) of q packed two to a word, plus one packed 16-bit add.
     uint32_t wh[4], wl[4];
-    if constexpr (FMT == IQK_IQ1_S_R4) {
-        // Four signed base-16 digits per value, q = d0 + 16 d1 + 256 d2 +
-        // 4096 d3 with d in [-8, 7]: the nibbles of the 16-bit q + 0x8888 are
-        // the digits plus 8.  Per group of eight values (h = 0: values 0-7,
-        // h = 1: 8-15) a plane word holds value j in nibble 2j and value
-        // 4 + j in nibble 2j + 1 (the grid entries' order); hi words
-        // [d0 h0, d0 h1, d1 h0, d1 h1], lo words the same for d2, d3.
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint32_t* qq = q + 8 * h;
-            // q + 0x8888 two to a word (each 16-bit lane stays in [0, 0xFFFF])
-            const uint32_t a0 = add_u16x2(__builtin_amdgcn_perm(qq[1], qq[0], 0x05040100u), 0x88888888u);
-            const uint32_t a1 = add_u16x2(__builtin_amdgcn_perm(qq[3], qq[2], 0x05040100u), 0x88888888u);
-            const uint32_t a2 = add_u16x2(__builtin_amdgcn_perm(qq[5], qq[4], 0x05040100u), 0x88888888u);
-            const uint32_t a3 = add_u16x2(__builtin_amdgcn_perm(qq[7], qq[6], 0x05040100u), 0x88888888u);
-            // low / high bytes of values 0-3 and 4-7; ^ 8 per nibble gives the digit
-            const uint32_t L0 = __builtin_amdgcn_perm(a1, a0, 0x06040200u) ^ 0x88888888u;
-            const uint32_t H0 = __builtin_amdgcn_perm(a1, a0, 0x07050301u) ^ 0x88888888u;
-            const uint32_t L1 = __builtin_amdgcn_perm(a3, a2, 0x06040200u) ^ 0x88888888u;
-            const uint32_t H1 = __builtin_amdgcn_perm(a3, a2, 0x07050301u) ^ 0x88888888u;
-            const uint32_t M = 0x0F0F0F0Fu;
-            wh[h] = (L0 & M) | ((L1 << 4) & ~M);
-            wh[2 + h] = ((L0 >> 4) & M) | (L1 & ~M);
-            wl[h] = (H0 & M) | ((H1 << 4) & ~M);
-            wl[2 + h] = ((H0 >> 4) & M) | (H1 & ~M);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // word j = values j, 4+j, 8+j, 12+j (the code-spread order)
-            const uint32_t w01 = __builtin_amdgcn_perm(q[j + 4], q[j], 0x05040100u);
-            const uint32_t w23 = __builtin_amdgcn_perm(q[j + 12], q[j + 8], 0x05040100u);
-            wl[j] = __builtin_amdgcn_perm(w23, w01, 0x06040200u);
-            wh[j] = __builtin_amdgcn_perm(add_u16x2(w23, 0x00800080u), add_u16x2(w01, 0x00800080u), 0x07050301u);
-        }
+    for (int j = 0; j < 4; ++j) {
+        // 2-bit members: word j = values j, 4+j, 8+j, 12+j (the code-spread order);
+        // IQ1_S_R4: natural order
+        const int i0 = FMT == IQK_IQ1_S_R4 ? 4 * j : j;
+        const int st = FMT == IQK_IQ1_S_R4 ? 1 : 4;
+        const uint32_t w01 = __builtin_amdgcn_perm(q[i0 + st], q[i0], 0x05040100u);
+        const uint32_t w23 = __builtin_amdgcn_perm(q[i0 + 3 * st], q[i0 + 2 * st], 0x05040100u);
+        wl[j] = __builtin_amdgcn_perm(w23, w01, 0x06040200u);
+        wh[j] = __builtin_amdgcn_perm(add_u16x2(w23, 0x00800080u), add_u16x2(w01, 0x00800080u), 0x07050301u);
     }
     const int slot = xslot(b >> 2, b & 3);
     *(uint4*)&L.hi[4 * slot] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
@@ -347,13 +319,6 @@ __device__ __forceinline__ void prep_block(const XRaw<XDT>& raw, XLds<N>& L, int
 __device__ __forceinline__ int dot4_first(uint32_t a, uint32_t b) {
     int d;
     asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
-    return d;
-}
-
-// d = dot8 of signed nibbles with the accumulator starting at zero
-__device__ __forceinline__ int dot8_first(uint32_t a, uint32_t b) {
-    int d;
-    asm("v_dot8_i32_i4 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
     return d;
 }
 
@@ -381,7 +346,7 @@ __device__ __forceinline__ int dot16(uint32_t qw, uint32_t m, uint32_t tlo, uint
 // the per-lane float scale (fp16 d * chunk scale * table scale).
 template <int FMT>
 __device__ __forceinline__ float row_dot(const RowData& r, int c, const uint32_t* xh, const uint32_t* xl,
-                                         const int32_t* bsum, uint32_t tlo, uint32_t thi, const uint32_t* grid_s) {
+                                         const int32_t* bsum, uint32_t tlo, uint32_t thi, const uint2* grid_s) {
     if constexpr (FMT == IQK_IQ2_K) {
         const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
         const uint32_t sc = r.a ^ 0x8888u;  // nibble ^ 8 read as signed 4-bit = nibble - 8
@@ -436,35 +401,25 @@ __device__ __forceinline__ float row_dot(const RowData& r, int c, const uint32_t
         }
         return (float)(ah * 256 + al);  // exact: |.| < 2^31, one rounding as before
     } else {
-        // group g = 4b + j: digit planes xh[4i + h], xh[4i + 2 + h], xl[4i + h],
-        // xl[4i + 2 + h] with i = g / 2, h = g % 2
         float part = 0.f;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const uint32_t h16 = (r.a >> (16 * b)) & 0xFFFFu;
             const uint32_t qsw = b == 0 ? r.q.x : r.q.y;
-            int a[4];
+            int ah = 0, al = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int g = 4 * b + j;
-                const int i = g >> 1, h = g & 1;
-                const uint32_t e = grid_s[((qsw >> (8 * j)) & 0xFFu) | (((h16 >> (3 * j)) & 7u) << 8)];
-                if (j == 0) {
-                    a[0] = dot8_first(e, xh[4 * i + h]);
-                    a[1] = dot8_first(e, xh[4 * i + 2 + h]);
-                    a[2] = dot8_first(e, xl[4 * i + h]);
-                    a[3] = dot8_first(e, xl[4 * i + 2 + h]);
-                } else {
-                    a[0] = __builtin_amdgcn_sdot8((int)e, (int)xh[4 * i + h], a[0], false);
-                    a[1] = __builtin_amdgcn_sdot8((int)e, (int)xh[4 * i + 2 + h], a[1], false);
-                    a[2] = __builtin_amdgcn_sdot8((int)e, (int)xl[4 * i + h], a[2], false);
-                    a[3] = __builtin_amdgcn_sdot8((int)e, (int)xl[4 * i + 2 + h], a[3], false);
-                }
+                const uint32_t idx = ((qsw >> (8 * j)) & 0xFFu) | (((h16 >> (3 * j)) & 7u) << 8);
+                const uint2 gv = grid_s[idx];
+                // (the chain's first dot starts from an inline zero: no v_mov)
+                ah = j == 0 ? dot4_first(gv.x, xh[2 * g]) : __builtin_amdgcn_sdot4((int)gv.x, (int)xh[2 * g], ah, false);
+                ah = __builtin_amdgcn_sdot4((int)gv.y, (int)xh[2 * g + 1], ah, false);
+                al = j == 0 ? dot4_first(gv.x, xl[2 * g]) : __builtin_amdgcn_sdot4((int)gv.x, (int)xl[2 * g], al, false);
+                al = __builtin_amdgcn_sdot4((int)gv.y, (int)xl[2 * g + 1], al, false);
             }
-            // exact integer sum of grid value * q over the block (|.| < 2^20)
-            const int dq = a[0] + a[1] * 16 + a[2] * 256 + a[3] * 4096;
             const float shift = (h16 >> 15) ? -0.125f : 0.125f;
-            const float tb = (float)dq + shift * (float)bsum[b];
+            const float tb = (float)(ah * 256 + al) + shift * (float)bsum[b];
             part += tb * (float)(2 * ((h16 >> 12) & 7u) + 1);
         }
         return part;
@@ -533,8 +488,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
     using G = Geo<N>;
     constexpr int kMaxX = max_x_rows<MODE>();
     __shared__ XLds<N> X[kMaxX];
-    // IQ1_S_R4 grid entry e: nibble 2j = value j, nibble 2j + 1 = value 4 + j
-    __shared__ uint32_t grid_s[FMT == IQK_IQ1_S_R4 ? 2048 : 1];
+    __shared__ uint2 grid_s[FMT == IQK_IQ1_S_R4 ? 2048 : 1];
 
     const int nthreads = blockDim.x;
     const int tid = threadIdx.x;
@@ -586,13 +540,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
     const int xtotal = nx * (N / 16);
     XRaw<XDT> xraw;
     if (tid < xtotal) xraw = load_xblock<N, XDT>(xrow_ptr(tid), tid % (N / 16));
-    uint4 gw0, gw1;  // two int8 grid entries each
+    uint4 gw0, gw1;
     const uint4* gsrc = (const uint4*)p.grid;
-    uint2* gdst = (uint2*)grid_s;
-    auto nib = [&](uint4 g) {
-        const uint32_t M4 = 0x0F0F0F0Fu;
-        return make_uint2((g.x & M4) | ((g.y & M4) << 4), (g.z & M4) | ((g.w & M4) << 4));
-    };
+    uint4* gdst = (uint4*)grid_s;
     if constexpr (FMT == IQK_IQ1_S_R4) {
         if (tid < 1024) gw0 = gsrc[tid];
         if (tid + nthreads < 1024) gw1 = gsrc[tid + nthreads];
@@ -611,9 +561,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_kernel(GemvParams p) {
     for (int i = tid + nthreads; i < xtotal; i += nthreads)
         prep_block<FMT, N, XDT>(load_xblock<N, XDT>(xrow_ptr(i), i % (N / 16)), X[i / (N / 16)], i % (N / 16));
     if constexpr (FMT == IQK_IQ1_S_R4) {
-        if (tid < 1024) gdst[tid] = nib(gw0);
-        if (tid + nthreads < 1024) gdst[tid + nthreads] = nib(gw1);
-        for (int i = tid + 2 * nthreads; i < 1024; i += nthreads) gdst[i] = nib(gsrc[i]);
+        if (tid < 1024) gdst[tid] = gw0;
+        if (tid + nthreads < 1024) gdst[tid + nthreads] = gw1;
+        for (int i = tid + 2 * nthreads; i < 1024; i += nthreads) gdst[i] = gsrc[i];
     }
     lds_barrier();
 
