@@ -144,6 +144,41 @@ def test_iq2k_hand_blocks():
     assert not np.any(np.signbit(w[b0 & (sb % 2 == 0)]))
 
 
+def test_iq2k_hand_block_stream_bytes():
+    # one row, n = 256 (one 76-byte wire block {d, extra, scales[8], qs[64]});
+    # the canonical streams are qs (64) | scl (8) | sex (2) | dv (2), each
+    # field at the position the stream table and the LSB-first reading give
+    wire = np.zeros(76, np.uint8)
+    wire[0:2] = [0x00, 0x3C]            # d = 1.0
+    wire[2:4] = [0x01, 0x80]            # extra: alphabet 1 for sub-blocks 0 and 15
+    wire[4:12] = 0x88                   # scale nibbles 8 (-> 0) ...
+    wire[4] = 0x21                      # ... sub-block 0: 1 (-> -7), sub-block 1: 2 (-> -6)
+    wire[11] = 0xF3                     # sub-block 14: 3 (-> -5), sub-block 15: 15 (-> 7)
+    wire[12 + 0] = 0x01                 # weight 0 (h=0, p=0, l=0): code 1
+    wire[12 + 5] = 0x08                 # weight 37 (h=0, p=1, l=5): code 2 at bits 2..3
+    wire[12 + 63] = 0xC0                # weight 255 (h=1, p=3, l=31): code 3 at bits 6..7
+    s = oracle.pack(K, wire, 1, 256)
+    expected = np.zeros(76, np.uint8)
+    expected[0] = 0x01                  # weight 0 -> qs byte 0, bits 0..1
+    expected[9] = 0x08                  # weight 37 -> qs byte 9, bits 2..3
+    expected[63] = 0xC0                 # weight 255 -> qs byte 63, bits 6..7
+    expected[64:72] = [0x21, 0x88, 0x88, 0x88, 0x88, 0x88, 0x88, 0xF3]  # scl: sub-block s at byte s/2, low nibble first
+    expected[72:74] = [0x01, 0x80]      # sex: bit s of the plane
+    expected[74:76] = [0x00, 0x3C]      # dv
+    assert np.array_equal(s, expected)
+    assert np.array_equal(oracle.unpack(K, s, 1, 256), wire)
+    values = np.array([1, 2, 3, 4, 5, 6, 7, 8], np.float32)
+    w = oracle.dequant(K, s, 1, 256, values)[0]
+    exp = np.zeros(256, np.float32)
+    exp[0:16] = -35.0                   # (1 * -7) * values[4 + 0]
+    exp[0] = -42.0                      # (1 * -7) * values[4 + 1]
+    exp[16:32] = -6.0                   # (1 * -6) * values[0]
+    exp[224:240] = -5.0                 # (1 * -5) * values[0]
+    exp[240:256] = 35.0                 # (1 * 7) * values[4 + 0]
+    exp[255] = 56.0                     # (1 * 7) * values[4 + 3]
+    assert np.array_equal(w, exp)
+
+
 def test_iq1s_r4_hand_group():
     # four rows, n = 32 (one block of four 8-weight groups)
     grid = np.zeros((2048, 8), np.int8)
