@@ -26,7 +26,7 @@ __all__ = [
     "IQ2_KS", "IQ2_K", "IQ1_S_R4", "IqkError", "IqkValueError", "Weights",
     "row_bytes", "plane_offsets", "pack_relayout", "unpack_relayout", "dequant", "moe_gemv",
     "route", "grouped_gemm", "prefill_workspace_bytes", "moe_prefill", "floor_gemv",
-    "floor_dequant", "stream_read", "library_path",
+    "floor_dequant", "stream_read", "stream_write", "library_path",
 ]
 
 IQ2_KS, IQ2_K, IQ1_S_R4 = 1, 2, 3
@@ -96,6 +96,7 @@ def _load():
         "iqk_floor_gemv": (i32, [W, p, p, p, i32, i32, p, i64, i32, p, p]),
         "iqk_floor_dequant": (i32, [W, i64, i64, i32, p, p]),
         "iqk_stream_read": (i32, [p, sz, p, sz, p]),
+        "iqk_stream_write": (i32, [p, sz, ctypes.c_uint32, p]),
         "iqk_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -129,7 +130,13 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def _dev(t: torch.Tensor | None, what: str, dtype=None):
+GRID_NUMEL = 2048 * 8  # the IQ1_S_R4 grid: 2048 entries of 8 int8 values
+
+
+def _dev(t: torch.Tensor | None, what: str, dtype=None, numel: int | None = None):
+    """Device pointer of a contiguous tensor, after checking its dtype and,
+    when `numel` is given, its element count (the kernels read or write
+    exactly that many elements; a shorter buffer would be overrun)."""
     if t is None:
         return None
     if not t.is_cuda:
@@ -138,7 +145,19 @@ def _dev(t: torch.Tensor | None, what: str, dtype=None):
         raise IqkValueError(_E_ARG, f"{what} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise IqkValueError(_E_ARG, f"{what} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise IqkValueError(_E_SIZE, f"{what} has {t.numel()} elements, expected {numel}")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _grid(grid: torch.Tensor | None):
+    return _dev(grid, "grid", torch.int8, GRID_NUMEL)
+
+
+def _ids(ids: torch.Tensor):
+    if ids.dim() != 2:
+        raise IqkValueError(_E_ARG, "ids must be [T, k]")
+    return _dev(ids, "ids", torch.int32)
 
 
 def _host_values(values):
@@ -208,8 +227,10 @@ def dequant(w: Weights, values=None, grid: torch.Tensor | None = None, out_dtype
         out = torch.empty((nrows, w.in_features), dtype=out_dtype, device=w.streams.device)
     _v, vp = _host_values(values)
     cw = w._c()
-    _check(_lib.iqk_dequant(ctypes.byref(cw), row0, nrows, vp, _dev(grid, "grid", torch.int8),
-                            _DT[out.dtype], _dev(out, "out"), _stream(stream)))
+    if out.dtype not in _DT:
+        raise IqkValueError(_E_ARG, "out must be float32, float16 or bfloat16")
+    _check(_lib.iqk_dequant(ctypes.byref(cw), row0, nrows, vp, _grid(grid),
+                            _DT[out.dtype], _dev(out, "out", numel=nrows * w.in_features), _stream(stream)))
     return out
 
 
@@ -230,8 +251,8 @@ def moe_gemv(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=None, grid: 
         y = torch.empty((T, k, w.out), dtype=torch.float32, device=w.streams.device)
     _v, vp = _host_values(values)
     cw = w._c()
-    _check(_lib.iqk_moe_gemv(ctypes.byref(cw), vp, _dev(grid, "grid", torch.int8), xp, xdt, x_slots,
-                             _dev(ids, "ids", torch.int32), T, k, _dev(y, "y", torch.float32), _stream(stream)))
+    _check(_lib.iqk_moe_gemv(ctypes.byref(cw), vp, _grid(grid), xp, xdt, x_slots,
+                             _ids(ids), T, k, _dev(y, "y", torch.float32, T * k * w.out), _stream(stream)))
     return y
 
 
@@ -245,8 +266,8 @@ def moe_gemv_swiglu(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=None,
         h = torch.empty((T, k, w.out // 2), dtype=torch.bfloat16, device=w.streams.device)
     _v, vp = _host_values(values)
     cw = w._c()
-    _check(_lib.iqk_moe_gemv_swiglu(ctypes.byref(cw), vp, _dev(grid, "grid", torch.int8), xp, xdt, x_slots,
-                                    _dev(ids, "ids", torch.int32), T, k, _dev(h, "h", torch.bfloat16),
+    _check(_lib.iqk_moe_gemv_swiglu(ctypes.byref(cw), vp, _grid(grid), xp, xdt, x_slots,
+                                    _ids(ids), T, k, _dev(h, "h", torch.bfloat16, T * k * (w.out // 2)),
                                     _stream(stream)))
     return h
 
@@ -263,9 +284,9 @@ def moe_gemv_combine(w: Weights, x: torch.Tensor, ids: torch.Tensor, route_w: to
         y = torch.empty((T, w.out), dtype=torch.float32, device=w.streams.device)
     _v, vp = _host_values(values)
     cw = w._c()
-    _check(_lib.iqk_moe_gemv_combine(ctypes.byref(cw), vp, _dev(grid, "grid", torch.int8), xp, xdt, x_slots,
-                                     _dev(ids, "ids", torch.int32), _dev(route_w, "route_w", torch.float32), T, k,
-                                     _dev(y, "y", torch.float32), _stream(stream)))
+    _check(_lib.iqk_moe_gemv_combine(ctypes.byref(cw), vp, _grid(grid), xp, xdt, x_slots,
+                                     _ids(ids), _dev(route_w, "route_w", torch.float32, T * k), T, k,
+                                     _dev(y, "y", torch.float32, T * w.out), _stream(stream)))
     return y
 
 
@@ -281,7 +302,7 @@ def moe_gemv_grouped(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=None
                      y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Grouped decode matvec: route, then one decode pass per selected expert
     shared by all of its pairs.  y[T, k, out] (float32); pairs with an
-    invalid id leave their rows untouched."""
+    invalid id get NaN rows."""
     T, k = ids.shape
     xp, xdt = _x_args(x, T, x_slots, w.in_features)
     if workspace is None:
@@ -290,10 +311,10 @@ def moe_gemv_grouped(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=None
         y = torch.zeros((T, k, w.out), dtype=torch.float32, device=w.streams.device)
     _v, vp = _host_values(values)
     cw = w._c()
-    _check(_lib.iqk_moe_gemv_grouped(ctypes.byref(cw), vp, _dev(grid, "grid", torch.int8), xp, xdt, x_slots,
-                                     _dev(ids, "ids", torch.int32), T, k, int(bool(sorted)),
+    _check(_lib.iqk_moe_gemv_grouped(ctypes.byref(cw), vp, _grid(grid), xp, xdt, x_slots,
+                                     _ids(ids), T, k, int(bool(sorted)),
                                      _dev(workspace, "workspace", torch.uint8), workspace.numel(),
-                                     _dev(y, "y", torch.float32), _stream(stream)))
+                                     _dev(y, "y", torch.float32, T * k * w.out), _stream(stream)))
     return y
 
 
@@ -306,7 +327,8 @@ def swiglu(y_gu: torch.Tensor, h: torch.Tensor | None = None, stream=None) -> to
     P = y_gu.numel() // (2 * I)
     if h is None:
         h = torch.empty((*y_gu.shape[:-1], I), dtype=torch.bfloat16, device=y_gu.device)
-    _check(_lib.iqk_swiglu(_dev(y_gu, "y_gu", torch.float32), P, I, _dev(h, "h", torch.bfloat16), _stream(stream)))
+    _check(_lib.iqk_swiglu(_dev(y_gu, "y_gu", torch.float32), P, I, _dev(h, "h", torch.bfloat16, P * I),
+                           _stream(stream)))
     return h
 
 
@@ -315,8 +337,8 @@ def combine(y: torch.Tensor, route_w: torch.Tensor, yc: torch.Tensor | None = No
     T, k, out = y.shape
     if yc is None:
         yc = torch.empty((T, out), dtype=torch.float32, device=y.device)
-    _check(_lib.iqk_combine(_dev(y, "y", torch.float32), _dev(route_w, "route_w", torch.float32), T, k, out,
-                            _dev(yc, "yc", torch.float32), _stream(stream)))
+    _check(_lib.iqk_combine(_dev(y, "y", torch.float32), _dev(route_w, "route_w", torch.float32, T * k), T, k, out,
+                            _dev(yc, "yc", torch.float32, T * out), _stream(stream)))
     return yc
 
 
@@ -340,9 +362,10 @@ def moe_auto(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=None, grid: 
     _v, vp = _host_values(values)
     cw = w._c()
     path = ctypes.c_int(-1)
-    _check(_lib.iqk_moe_auto(ctypes.byref(cw), vp, _dev(grid, "grid", torch.int8), xp, xdt, x_slots,
-                             _dev(ids, "ids", torch.int32), T, k, _dev(workspace, "workspace", torch.uint8),
-                             workspace.numel(), _dev(y, "y", torch.float32), ctypes.byref(path), _stream(stream)))
+    _check(_lib.iqk_moe_auto(ctypes.byref(cw), vp, _grid(grid), xp, xdt, x_slots,
+                             _ids(ids), T, k, _dev(workspace, "workspace", torch.uint8),
+                             workspace.numel(), _dev(y, "y", torch.float32, T * k * w.out), ctypes.byref(path),
+                             _stream(stream)))
     return y, AUTO_PATHS[path.value]
 
 
@@ -355,8 +378,8 @@ def floor_gemv(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=None, grid
         sink = torch.empty((T, k, w.out), dtype=torch.int32, device=w.streams.device)
     _v, vp = _host_values(values)
     cw = w._c()
-    _check(_lib.iqk_floor_gemv(ctypes.byref(cw), vp, _dev(grid, "grid", torch.int8), xp, xdt, x_slots,
-                               _dev(ids, "ids", torch.int32), T, k, _dev(sink, "sink", torch.int32),
+    _check(_lib.iqk_floor_gemv(ctypes.byref(cw), vp, _grid(grid), xp, xdt, x_slots,
+                               _ids(ids), T, k, _dev(sink, "sink", torch.int32, T * k * w.out),
                                _stream(stream)))
     return sink
 
@@ -367,7 +390,10 @@ def floor_dequant(w: Weights, out_dtype=torch.bfloat16, row0: int = 0, nrows: in
     if out is None:
         out = torch.empty((nrows, w.in_features), dtype=out_dtype, device=w.streams.device)
     cw = w._c()
-    _check(_lib.iqk_floor_dequant(ctypes.byref(cw), row0, nrows, _DT[out.dtype], _dev(out, "out"), _stream(stream)))
+    if out.dtype not in _DT:
+        raise IqkValueError(_E_ARG, "out must be float32, float16 or bfloat16")
+    _check(_lib.iqk_floor_dequant(ctypes.byref(cw), row0, nrows, _DT[out.dtype],
+                                  _dev(out, "out", numel=nrows * w.in_features), _stream(stream)))
     return out
 
 
@@ -376,6 +402,14 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> torch.Ten
     _check(_lib.iqk_stream_read(_dev(buf, "buf"), nbytes, _dev(sink, "sink", torch.int32), sink.numel(),
                                 _stream(stream)))
     return sink
+
+
+def stream_write(buf: torch.Tensor, value: int = 0, stream=None) -> torch.Tensor:
+    """Plain streaming write of `value` into every 32-bit word of buf (the
+    write ceiling of the dequantization producer)."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(_lib.iqk_stream_write(_dev(buf, "buf"), nbytes, int(value) & 0xFFFFFFFF, _stream(stream)))
+    return buf
 
 
 def route(ids: torch.Tensor, E: int, sorted: bool = False, stream=None):
@@ -398,9 +432,11 @@ def grouped_gemm(W: torch.Tensor, x: torch.Tensor, T: int, k: int, offsets: torc
         raise IqkValueError(_E_SIZE, "x must be bf16 [T, x_slots, in]")
     if y is None:
         y = torch.zeros((T, k, out), dtype=torch.float32, device=W.device)
+    if perm.numel() < T * k:
+        raise IqkValueError(_E_SIZE, f"perm has {perm.numel()} elements, expected at least T*k = {T * k}")
     _check(_lib.iqk_grouped_gemm(_dev(W, "W", torch.bfloat16), E, out, n, _dev(x, "x"), x_slots, T, k,
-                                 _dev(offsets, "offsets", torch.int32), _dev(perm, "perm", torch.int32),
-                                 _dev(y, "y", torch.float32), _stream(stream)))
+                                 _dev(offsets, "offsets", torch.int32, E + 1), _dev(perm, "perm", torch.int32),
+                                 _dev(y, "y", torch.float32, T * k * out), _stream(stream)))
     return y
 
 
@@ -424,10 +460,10 @@ def moe_prefill(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=None, gri
         y = torch.zeros((T, k, w.out), dtype=torch.float32, device=w.streams.device)
     _v, vp = _host_values(values)
     cw = w._c()
-    _check(_lib.iqk_moe_prefill(ctypes.byref(cw), vp, _dev(grid, "grid", torch.int8), _dev(x, "x"), x_slots,
-                                _dev(ids, "ids", torch.int32), T, k, int(bool(sorted)),
+    _check(_lib.iqk_moe_prefill(ctypes.byref(cw), vp, _grid(grid), _dev(x, "x"), x_slots,
+                                _ids(ids), T, k, int(bool(sorted)),
                                 _dev(workspace, "workspace", torch.uint8), workspace.numel(),
-                                _dev(y, "y", torch.float32), _stream(stream)))
+                                _dev(y, "y", torch.float32, T * k * w.out), _stream(stream)))
     return y
 
 
@@ -452,8 +488,8 @@ def moe_prefill_fused(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=Non
         y = torch.zeros((T, k, w.out), dtype=torch.float32, device=w.streams.device)
     _v, vp = _host_values(values)
     cw = w._c()
-    _check(_lib.iqk_moe_prefill_fused(ctypes.byref(cw), vp, _dev(grid, "grid", torch.int8), _dev(x, "x"), x_slots,
-                                      _dev(ids, "ids", torch.int32), T, k, int(bool(sorted)),
+    _check(_lib.iqk_moe_prefill_fused(ctypes.byref(cw), vp, _grid(grid), _dev(x, "x"), x_slots,
+                                      _ids(ids), T, k, int(bool(sorted)),
                                       _dev(workspace, "workspace", torch.uint8), workspace.numel(),
-                                      _dev(y, "y", torch.float32), _stream(stream)))
+                                      _dev(y, "y", torch.float32, T * k * w.out), _stream(stream)))
     return y

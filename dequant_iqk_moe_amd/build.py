@@ -27,6 +27,8 @@ PER_FILE = {
     "iqk_fused.hip": [],
     "iqk_glue.hip": [],
     "iqk_host.cpp": [],
+    "iqk_relayout.cpp": [],
+    "iqk_status.cpp": [],
 }
 
 

@@ -367,14 +367,23 @@ __global__ __launch_bounds__(kThreads) void dequant_wide_kernel(DequantParams p)
     const int lane = tid & 63;
     const int wave = tid >> 6;
     if (tid < 8) tab[tid] = p.values[tid];
+    // f16 / bf16 output of IQ1_S_R4 looks each weight up among the three
+    // values a ternary grid gives; a grid holding any other value makes the
+    // whole output NaN (checked while the grid is staged)
+    constexpr bool kTernary = FMT == IQK_IQ1_S_R4 && OUT_DT != IQK_F32 && !FLOOR;
+    uint32_t off_grid = 0;
     if constexpr (FMT == IQK_IQ1_S_R4) {
         if (!FLOOR) {
             const uint4* src = (const uint4*)p.grid;
             uint4* dst = (uint4*)grid_s;
-            for (int i = tid; i < 1024; i += kThreads) dst[i] = src[i];
+            for (int i = tid; i < 1024; i += kThreads) {
+                const uint4 v = src[i];
+                dst[i] = v;
+                if constexpr (kTernary) off_grid |= non_ternary(v.x) | non_ternary(v.y) | non_ternary(v.z) | non_ternary(v.w);
+            }
         }
     }
-    __syncthreads();
+    const bool nan_out = kTernary ? __syncthreads_or(off_grid != 0) != 0 : (__syncthreads(), false);
 
     const int64_t cpr = p.ipr;                 // chunks per row
     const int64_t chunks = p.nrows * cpr;
@@ -393,6 +402,10 @@ __global__ __launch_bounds__(kThreads) void dequant_wide_kernel(DequantParams p)
         if (ch < chunks) {
             uint32_t o[WS::WORDS];
             decode_chunk<FMT, OUT_DT, FLOOR>(p, p.row0 + lr, col, tab, grid_s, o);
+            if (kTernary && nan_out) {
+#pragma unroll
+                for (int i = 0; i < WS::WORDS; ++i) o[i] = OUT_DT == IQK_F16 ? 0x7E007E00u : 0x7FC07FC0u;
+            }
 #pragma unroll
             for (int i = 0; i < WS::WORDS / 4; ++i) *(uint4*)(my + 16 * i) = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
         }

@@ -8,9 +8,11 @@
 // into MFMA operand registers, so each expert's compressed rows are read
 // once and the 2-byte-per-weight round trip through HBM disappears.  The
 // weights are the ones iqk_dequant writes ("Format": d * float(scale) *
-// table value, or d * float(2 ls + 1) * (grid value + shift), float32, then
-// one round-to-nearest-even cast to bf16; every such product is exact in
-// float32, so the order of the two multiplications does not matter).
+// table value, or d * float(2 ls + 1) * (grid value + shift), float32, the
+// two multiplications in that order, each rounded, then one
+// round-to-nearest-even cast to bf16).  The IQ1_S_R4 grid must be ternary,
+// as the grid is defined: a block's weights are looked up among the three
+// values it can take; a grid holding any other value makes the output NaN.
 //
 // gfx950 design.
 //   * A workgroup owns one expert and 256 weight rows; each of its 16 waves
@@ -314,7 +316,7 @@ __device__ __forceinline__ void stage_tokens(const FusedParams& p, FusedShared<F
 template <int FMT, int N, int MT>
 __device__ __forceinline__ void fused_pass(const FusedParams& p, FusedShared<FMT, N>& sh, const ExpertRes& res,
                                            const Table8& tv, int base, int M, int tb,
-                                           int rb0, int rb1, int tid, int li, int g, int wave) {
+                                           int rb0, int rb1, int tid, int li, int g, int wave, bool nan_out) {
     constexpr int KC = MT == 1 ? (N < kFKC1 ? N : kFKC1) : (N < 2048 ? N : 2048);
     constexpr int PITCH = 2 * KC + kFPad;  // LDS row pitch
     constexpr int SSC = KC / 512;          // super-steps per chunk
@@ -336,7 +338,7 @@ __device__ __forceinline__ void fused_pass(const FusedParams& p, FusedShared<FMT
                 const int ti = tb + 16 * m + 4 * g + i;
                 const bool ok = ti < M && row < p.out;
                 const int pr = p.perm[base + (ok ? ti : 0)];
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[m][i]), yres,
+                __builtin_amdgcn_raw_buffer_store_b32(nan_out ? 0x7FC00000u : __float_as_uint(acc[m][i]), yres,
                                                       ok ? (uint32_t)((pr * p.out + row) * 4) : kOob, 0, 0);
             }
         }
@@ -493,14 +495,20 @@ __global__ __launch_bounds__(kFThreads) void fused_prefill_kernel(FusedParams p)
     const int64_t lo = C * blockIdx.x / gridDim.x, hi = C * (blockIdx.x + 1) / gridDim.x;
     if (lo >= hi) return;
 
+    uint32_t off_grid = 0;
     if constexpr (FMT == IQK_IQ1_S_R4) {
-        for (int i = tid; i < 1024; i += kFThreads) ((uint4*)sh.grid)[i] = ((const uint4*)p.grid)[i];
+        for (int i = tid; i < 1024; i += kFThreads) {
+            const uint4 v = ((const uint4*)p.grid)[i];
+            ((uint4*)sh.grid)[i] = v;
+            off_grid |= non_ternary(v.x) | non_ternary(v.y) | non_ternary(v.z) | non_ternary(v.w);
+        }
     }
     if (tid < 8) sh.tab[tid] = p.tab[tid];
     // the expert whose cost range holds lo (exactly one: plan is non-decreasing, plan[0] = 0 <= lo < C)
     for (int e = tid; e < p.E; e += kFThreads)
         if (p.plan[e] <= lo && p.plan[e + 1] > lo) e_first = e;
-    __syncthreads();
+    // a grid value outside {-1, 0, +1}: every output of the block is NaN
+    const bool nan_out = __syncthreads_or(off_grid != 0) != 0;
     // the value table in vector registers (the alphabet select needs them there)
     const Table8 tv{sh.tab[0], sh.tab[1], sh.tab[2], sh.tab[3], sh.tab[4], sh.tab[5], sh.tab[6], sh.tab[7]};
 
@@ -539,8 +547,8 @@ __global__ __launch_bounds__(kFThreads) void fused_prefill_kernel(FusedParams p)
             const int M = p.offsets[e + 1] - base;
             const ExpertRes res = expert_res<FMT, N>(p, e);
             for (int tb = 0; tb < M; tb += 16 * kFMT) {
-                if (M - tb > 16) fused_pass<FMT, N, 2>(p, sh, res, tv, base, M, tb, rb0, rb1, tid, li, g, wave);
-                else fused_pass<FMT, N, 1>(p, sh, res, tv, base, M, tb, rb0, rb1, tid, li, g, wave);
+                if (M - tb > 16) fused_pass<FMT, N, 2>(p, sh, res, tv, base, M, tb, rb0, rb1, tid, li, g, wave, nan_out);
+                else fused_pass<FMT, N, 1>(p, sh, res, tv, base, M, tb, rb0, rb1, tid, li, g, wave, nan_out);
             }
         }
         if (!go_on) break;

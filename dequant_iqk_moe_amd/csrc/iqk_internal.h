@@ -7,50 +7,17 @@
 #include <stdint.h>
 
 #include "../../include/iqk.h"
+#include "iqk_layout.h"
 
 namespace iqk {
 
-// Plane byte offsets of an R-row canonical stream tensor (see iqk.h).
-struct Planes {
-    int64_t off[5];
-    int64_t total;
-};
-
-inline bool shape_ok(int fmt, int64_t n) {
-    if (n <= 0) return false;
-    if (fmt == IQK_IQ2_KS || fmt == IQK_IQ2_K) return n % 256 == 0;
-    if (fmt == IQK_IQ1_S_R4) return n % 32 == 0;
-    return false;
+// Nonzero when a byte of w is not -1, 0 or +1 (0xFF, 0x00, 0x01), the
+// values of the IQ1_S_R4 grid: those are the bytes whose bits 1..7 are all
+// equal, except -2 (bits 1..7 set, bit 0 clear).
+__device__ __forceinline__ uint32_t non_ternary(uint32_t w) {
+    return ((w ^ (w >> 1)) & 0x7E7E7E7Eu) | (w & ~(w << 7) & 0x80808080u);
 }
 
-inline int64_t row_bytes(int fmt, int64_t n) {
-    if (fmt == IQK_IQ2_KS) return 2 + 70 * n / 256;
-    if (fmt == IQK_IQ2_K) return 76 * n / 256;
-    return 2 + 6 * n / 32;
-}
-
-inline Planes planes(int fmt, int64_t R, int64_t n) {
-    Planes p;
-    for (int i = 0; i < 5; ++i) p.off[i] = -1;
-    if (fmt == IQK_IQ2_KS) {
-        p.off[0] = 0;                       // qs
-        p.off[1] = p.off[0] + R * n / 4;    // scl
-        p.off[2] = p.off[1] + R * n / 64;   // sch
-        p.off[3] = p.off[2] + R * n / 256;  // sex
-        p.off[4] = p.off[3] + R * n / 256;  // dv
-    } else if (fmt == IQK_IQ2_K) {
-        p.off[0] = 0;                       // qs
-        p.off[1] = p.off[0] + R * n / 4;    // scl
-        p.off[2] = p.off[1] + R * n / 32;   // sex
-        p.off[3] = p.off[2] + R * n / 128;  // dv
-    } else {
-        p.off[0] = 0;                       // qs
-        p.off[1] = p.off[0] + R * n / 8;    // qh
-        p.off[2] = p.off[1] + R * (n / 32) * 2;  // dv
-    }
-    p.total = R * row_bytes(fmt, n);
-    return p;
-}
 
 // Dequantization / producer launch description.
 struct DequantLaunch {
@@ -88,8 +55,10 @@ struct GemvLaunch {
 struct RouteLaunch {
     const int32_t* ids;
     int64_t P, E;
-    int sorted;
+    int sorted;  // 1: the caller states ids are non-decreasing (checked; the ranking is skipped when they are)
     int32_t *counts, *offsets, *perm;
+    float* ynan = nullptr;  // if set: rows [P, yout] of the call's output, NaN for pairs with an invalid id
+    int64_t yout = 0;
 };
 
 struct GemmLaunch {
@@ -130,5 +99,6 @@ hipError_t launch_grouped_gemm(const GemmLaunch& a, hipStream_t s);
 hipError_t launch_swiglu(const float* y_gu, int64_t P, int64_t I, uint16_t* h, hipStream_t s);
 hipError_t launch_combine(const float* y, const float* w, int64_t T, int k, int64_t out, float* yc, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, hipStream_t s);
+hipError_t launch_stream_write(void* buf, size_t bytes, uint32_t value, hipStream_t s);
 
 }  // namespace iqk

@@ -7,9 +7,13 @@
 //
 // Routing: one workgroup builds per-expert counts (LDS atomics), an
 // exclusive scan, and a stable expert-major permutation of the pairs; the
-// stable scatter runs in one wave, 64 pairs at a time, ranking equal ids
-// inside the wave with ballots so the order inside an expert is the pair
-// order.
+// stable scatter ranks 64 pairs at a time per wave, equal ids found with
+// ballots, so the order inside an expert is the pair order.  When the caller
+// states that the ids are sorted and the histogram pass confirms they are
+// non-decreasing, the stable sort is the identity on the valid pairs and the
+// ranking is skipped.  Pairs with an id outside [0, E) are dropped; when the
+// caller passes its output, their rows are set to NaN here (the prefill and
+// grouped kernels only write the rows of routed pairs).
 //
 // Grouped GEMM: per expert e with M_e routed pairs, Y_e = X_e W_e^T with bf16
 // inputs and float32 accumulation on v_mfma_f32_16x16x32_bf16.  A workgroup
@@ -37,21 +41,48 @@ constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kRouteHistE = 1024;  // experts up to which the waves rank in parallel
 
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids, int32_t P, int32_t E,
-                                                              int32_t* __restrict__ counts,
+                                                              int32_t sorted, int32_t* __restrict__ counts,
                                                               int32_t* __restrict__ offsets,
-                                                              int32_t* __restrict__ perm) {
+                                                              int32_t* __restrict__ perm, float* __restrict__ ynan,
+                                                              int32_t yout) {
     __shared__ int32_t cur[kRouteMaxE];
     __shared__ int32_t part[kRouteThreads];
     __shared__ int32_t stage[kRouteStage];
     __shared__ int32_t hist[kRouteWaves * kRouteHistE];  // per-wave expert counts, then starts
+    __shared__ int32_t n_bad, n_neg;                      // invalid ids, ids below zero
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += kRouteThreads) cur[e] = 0;
+    if (tid == 0) n_bad = n_neg = 0;
     __syncthreads();
+    int descents = 0;  // ids[p - 1] > ids[p] seen by this thread (checked only for a sorted call)
     for (int p = tid; p < P; p += kRouteThreads) {
         const int e = ids[p];
-        if (e >= 0 && e < E) atomicAdd(&cur[e], 1);
+        if (e >= 0 && e < E) {
+            atomicAdd(&cur[e], 1);
+        } else {
+            atomicAdd(&n_bad, 1);
+            if (e < 0) atomicAdd(&n_neg, 1);
+        }
+        if (sorted && p > 0 && ids[p - 1] > e) descents = 1;
     }
-    __syncthreads();
+    // (the barrier after the histogram, taken by every thread whatever the flag)
+    const bool any_descent = __syncthreads_or(descents) != 0;
+    const bool identity = sorted && !any_descent;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    if (ynan && n_bad > 0) {
+        // NaN rows for the dropped pairs, one wave per pair
+        for (int p0 = wave * 64; p0 < P; p0 += kRouteThreads) {
+            const int e = p0 + lane < P ? ids[p0 + lane] : 0;
+            uint64_t m = __ballot(e < 0 || e >= E);
+            while (m) {
+                const int pp = p0 + __builtin_ctzll(m);
+                m &= m - 1;
+                float* row = ynan + (int64_t)pp * yout;
+                for (int o = lane; o < yout; o += 64) row[o] = __builtin_nanf("");
+            }
+        }
+    }
     // exclusive scan: each thread owns a contiguous segment of experts
     const int seg = (E + kRouteThreads - 1) / kRouteThreads;
     const int e0 = min(tid * seg, E), e1 = min(e0 + seg, E);
@@ -77,6 +108,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
     const int total = part[kRouteThreads - 1];
     // positions past the valid pairs (invalid ids are dropped)
     for (int p = total + tid; p < P; p += kRouteThreads) perm[p] = -1;
+    if (identity) {
+        // non-decreasing ids: ids below zero come first, ids >= E last, and
+        // the valid pairs in between are already in stable expert order
+        const int first = n_neg;
+        for (int i = tid; i < total; i += kRouteThreads) perm[i] = first + i;
+        return;
+    }
     // stable scatter.  The ids are staged in LDS a chunk at a time.  Up to
     // kRouteHistE experts, each wave takes a contiguous slice of the chunk:
     // per-wave expert counts, an exclusive prefix over the waves gives each
@@ -85,8 +123,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
     // pairs per step, equal ids found with one ballot per id bit.
     int nbits = 1;
     while ((1 << nbits) < E) ++nbits;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
     const uint64_t lt = (1ull << lane) - 1ull;
     const bool waves_split = E <= kRouteHistE;
     // ranks the pairs [i0, i1) of the staged chunk against the cursors cur_w
@@ -279,12 +315,30 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
     if ((threadIdx.x & 63) == 0) sink[((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) % sink_words] = acc;
 }
 
+// plain streaming write (HBM write-ceiling reference): the value in every
+// 16-byte word, non-temporal 16-byte stores, a wave covering 1 KiB per store
+// instruction as the dequantization producer's stores do
+__global__ __launch_bounds__(256) void stream_write_kernel(u32x4* __restrict__ buf, int64_t n16, uint32_t value) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    const u32x4 v = {value, value, value, value};
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) __builtin_nontemporal_store(v, buf + i);
+}
+
 }  // namespace
+
+hipError_t launch_stream_write(void* buf, size_t bytes, uint32_t value, hipStream_t s) {
+    const int64_t n16 = (int64_t)(bytes / 16);
+    int64_t blocks = (n16 + 255) / 256;
+    blocks = blocks < 256 * 512 ? blocks : 256 * 512;  // the producer's launch cap
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(stream_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (u32x4*)buf, n16, value);
+    return hipGetLastError();
+}
 
 hipError_t launch_route(const RouteLaunch& a, hipStream_t s) {
     if (a.E > kRouteMaxE) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, a.ids, (int32_t)a.P, (int32_t)a.E, a.counts,
-                       a.offsets, a.perm);
+    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, a.ids, (int32_t)a.P, (int32_t)a.E,
+                       (int32_t)a.sorted, a.counts, a.offsets, a.perm, a.ynan, (int32_t)a.yout);
     return hipGetLastError();
 }
 

@@ -125,11 +125,13 @@ int iqk_unpack_relayout(int fmt, const uint8_t* streams, size_t streams_bytes, i
  * unspecified payload).
  * `values`: host float[8] for the 2-bit members (any float32 values),
  * ignored for IQ1_S_R4.  `grid`: device int8[2048*8] (row idx = 8 grid
- * values) for IQ1_S_R4, ignored otherwise; its values are ternary
- * (-1, 0, +1, the grid's definition): the f16 / bf16 outputs look each
- * weight up among the three rounded values a block can take, so any other
- * grid value gives an unspecified result there (float32 output computes
- * every weight). */
+ * values) for IQ1_S_R4, ignored otherwise.  Precondition of the f16 / bf16
+ * output when in % 64 == 0: the grid is ternary (-1, 0, +1, the grid's
+ * definition), since each weight is looked up among the three rounded
+ * values its block can take; the kernel checks the grid as it loads it and
+ * writes NaN to every output if any value is outside {-1, 0, +1}.  The
+ * float32 output (and f16 / bf16 at other widths) computes any int8 grid
+ * value. */
 int iqk_dequant(const iqk_weights* w, int64_t row0, int64_t nrows, const float* values,
                 const int8_t* grid, int out_dtype, void* out, void* stream);
 
@@ -139,7 +141,8 @@ int iqk_dequant(const iqk_weights* w, int64_t row0, int64_t nrows, const float* 
  * input, down).  x: device [T, x_slots, in] of x_dtype IQK_F32 or IQK_BF16,
  * finite (a NaN or infinite activation gives an unspecified result).
  * ids: device int32 [T, k]; an id outside [0, experts) gives a NaN output
- * row.  y: device float32 [T, k, out].
+ * row (the rule of every routed-product call of this library).
+ * y: device float32 [T, k, out].
  * Widths: in must be 512, 2048 or 4096 (IQK_E_WIDTH otherwise): a kernel
  * instance makes exactly one pass over k.  The values table (host float[8])
  * must be m_i * 2^e with integer |m_i| <= 127 for one common e (integer
@@ -190,10 +193,9 @@ int iqk_moe_gemv_grouped_workspace(const iqk_weights* w, int64_t T, int k, size_
  * tokens is read and decoded once per pass.  Arguments, value-table rule, accuracy
  * and widths as iqk_moe_gemv; workspace from iqk_moe_gemv_grouped_workspace;
  * `sorted` as iqk_route.  Per pair the sums are formed as in iqk_moe_gemv
- * (the two agree to float32 rounding).  Pairs with an invalid id leave
- * their rows of y untouched (they are dropped by the routing, as in the
- * prefill calls).  Limits: as iqk_moe_gemv, E <= 16384, T * k * out * 4 <
- * 2^31. */
+ * (the two agree to float32 rounding).  Pairs with an invalid id get NaN
+ * rows, as in iqk_moe_gemv (the routing drops them and writes those rows).
+ * Limits: as iqk_moe_gemv, E <= 16384, T * k * out * 4 < 2^31. */
 int iqk_moe_gemv_grouped(const iqk_weights* w, const float* values, const int8_t* grid,
                          const void* x, int x_dtype, int x_slots, const int32_t* ids,
                          int64_t T, int k, int sorted, void* workspace, size_t ws_bytes,
@@ -213,8 +215,7 @@ int iqk_moe_auto_workspace(const iqk_weights* w, int64_t T, int k, size_t* bytes
  * when x is bf16 (else IQK_E_TABLE).  *path (if non-null) receives 0, 1 or
  * 2 for the path taken.  Arguments and errors are those of the chosen call;
  * accuracy is that call's (1e-3 for the matvecs, 2e-2 for the prefill).  Rows
- * of pairs with an invalid id are left as they were or set to NaN,
- * depending on the path. */
+ * of pairs with an invalid id are NaN on every path. */
 int iqk_moe_auto(const iqk_weights* w, const float* values, const int8_t* grid,
                  const void* x, int x_dtype, int x_slots, const int32_t* ids, int64_t T, int k,
                  void* workspace, size_t ws_bytes, float* y, int* path, void* stream);
@@ -242,8 +243,11 @@ int iqk_combine(const float* y, const float* route_w, int64_t T, int k, int64_t 
  * sum) and perm[P]: pair indices grouped by increasing expert, increasing
  * pair index inside an expert (a stable sort); pairs with an id outside
  * [0, E) are dropped and the remaining perm entries are set to -1.
- * `sorted` = 1 states that ids are already non-decreasing (the caller's
- * sort flag); the result is the same either way.  P <= 2^24, E <= 16384. */
+ * `sorted` = 1 is the caller's sort flag ("Surface"): it states that ids
+ * are non-decreasing, in which case the stable sort is the identity on the
+ * valid pairs and the kernel skips the ranking.  The kernel confirms the
+ * order while it counts (ids not in order take the full ranking), so the
+ * result is the same either way.  P <= 2^24, E <= 16384. */
 int iqk_route(const int32_t* ids, int64_t P, int64_t E, int sorted,
               int32_t* counts, int32_t* offsets, int32_t* perm, void* stream);
 
@@ -271,7 +275,8 @@ int iqk_moe_prefill_fused_workspace(const iqk_weights* w, int64_t T, int k, size
  * gathered bf16 token rows, float32 accumulation.  Arguments as
  * iqk_moe_prefill (workspace from iqk_moe_prefill_fused_workspace); the
  * value table may be any float32 values; the IQ1_S_R4 grid must be
- * ternary as for iqk_dequant's f16 / bf16 output.  Widths: in = 512, 2048
+ * ternary as for iqk_dequant's f16 / bf16 output (checked as the grid is
+ * loaded: any other value makes every output row of the call NaN).  Widths: in = 512, 2048
  * or 4096 (IQK_E_WIDTH otherwise); out * iqk_row_bytes(fmt, in) < 2^31.
  * Accuracy: as iqk_moe_prefill (2e-2 against the float32-weight product;
  * the result differs from iqk_moe_prefill only in summation order). */
@@ -286,9 +291,10 @@ int iqk_moe_prefill_workspace(const iqk_weights* w, int64_t T, int k, size_t* by
 /* Prefill ("Surface": many pairs): iqk_route, then iqk_dequant of all
  * experts to bf16 in the workspace ("dequantizes the stacked experts in one
  * kernel pass"), then iqk_grouped_gemm.  x: device bf16 [T, x_slots, in];
- * y: device float32 [T, k, out]; invalid ids leave their rows untouched.
+ * y: device float32 [T, k, out]; invalid ids give NaN rows.
  * Accuracy against the float32-weight product: ||y - y_exact|| /
- * ||y_exact|| <= 2e-2 (bf16 weights). */
+ * ||y_exact|| <= 2e-2 (bf16 weights).  Invalid ids give NaN rows; the
+ * output is float32 (an out_dtype argument is not provided). */
 int iqk_moe_prefill(const iqk_weights* w, const float* values, const int8_t* grid,
                     const void* x_bf16, int x_slots, const int32_t* ids, int64_t T, int k,
                     int sorted, void* workspace, size_t ws_bytes, float* y, void* stream);
@@ -310,6 +316,10 @@ int iqk_floor_gemv(const iqk_weights* w, const float* values, const int8_t* grid
 int iqk_floor_dequant(const iqk_weights* w, int64_t row0, int64_t nrows, int out_dtype,
                       void* out, void* stream);
 int iqk_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, void* stream);
+/* Plain HBM streaming write (the write ceiling the dequantization producer
+ * is measured against): `value` in every 32-bit word of `bytes` (a
+ * multiple of 16) of device memory at `buf`, non-temporal 16-byte stores. */
+int iqk_stream_write(void* buf, size_t bytes, uint32_t value, void* stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* iqk_last_error(void);

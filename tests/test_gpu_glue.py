@@ -1,8 +1,8 @@
 """GPU parity of the MoE-layer glue entry points against the oracle.
 
-iqk_moe_gemv_swiglu: h = silu(gate . x) * (up . x) stored as bf16; bar:
-per-vector relative error <= 5e-3 (bf16 storage is a half-ulp of 2^-9
-relative on top of the matvec's 1e-3).  iqk_moe_gemv_combine:
+iqk_moe_gemv_swiglu: h = silu(gate . x) * (up . x) stored as bf16; bar: the
+matvec's 1e-3 per vector on top of the bf16 cast's exact allowance of half a
+bf16 spacing per element (``gpu_common.bf16_storage_excess``).  iqk_moe_gemv_combine:
 y[t] = sum_j w[t, j] W_j x_j in float32; bar: |y - ref| <= 1e-3 *
 sum_j |w_j| ||W_j x_j|| per token (the combine may cancel, so the bound is
 taken on the parts)."""
@@ -13,12 +13,11 @@ import torch
 import oracle
 import synth
 import dequant_iqk_moe_amd as q
-from gpu_common import TOL_GEMV, announce, bf16_round, rel_err_per_vector, to_dev
+from gpu_common import TOL_GEMV, announce, bf16_round, bf16_storage_excess, to_dev
 
 pytestmark = pytest.mark.gpu
 
 KS, K, R4 = 1, 2, 3
-TOL_SWIGLU = 5e-3
 
 
 def _weights(fmt, E, out, n, seed):
@@ -49,8 +48,8 @@ def test_swiglu_parity(fmt, n, I, T, k, E, x_slots):
     h = h.float().cpu().numpy()
     ref = oracle.swiglu(oracle.moe(fmt, s, E, 2 * I, n, x, ids, values, grid, x_slots=x_slots))
     assert h.shape == (T, k, I)
-    err = rel_err_per_vector(h, ref)
-    assert np.all(err <= TOL_SWIGLU), err.max()
+    err = bf16_storage_excess(h, ref)
+    assert np.all(err <= TOL_GEMV), err.max()
 
 
 @pytest.mark.parametrize("fmt", [KS, K, R4])
@@ -107,7 +106,7 @@ def test_swiglu_invalid_ids_give_nan_rows():
     h = q.moe_gemv_swiglu(w, to_dev(x, torch.bfloat16), to_dev(ids), values).float().cpu().numpy()
     assert np.all(np.isnan(h[0, 1])) and np.all(np.isnan(h[0, 2]))
     ref = oracle.swiglu(oracle.moe(fmt, s, E, 2 * I, n, x, ids, values))
-    assert np.all(rel_err_per_vector(h[0, [0, 3]], ref[0, [0, 3]]) <= TOL_SWIGLU)
+    assert np.all(bf16_storage_excess(h[0, [0, 3]], ref[0, [0, 3]]) <= TOL_GEMV)
 
 
 # ---------------------------------------------------------------------------
@@ -125,7 +124,7 @@ def test_standalone_swiglu_matches_oracle_and_the_epilogue():
     announce("standalone swiglu")
     h = q.swiglu(to_dev(y)).float().cpu().numpy()
     ref = oracle.swiglu(y.astype(np.float64))
-    assert np.all(rel_err_per_vector(h, ref) <= TOL_SWIGLU)
+    assert np.all(bf16_storage_excess(h, ref) <= TOL_GEMV)
     # against the epilogue: the same gate/up sums through either route
     fmt, n, I2, E, T, k = K, 2048, 64, 8, 3, 6
     w, s = _weights(fmt, E, 2 * I2, n, 1001)
