@@ -85,6 +85,7 @@ def _load():
         "iqk_moe_gemv_grouped": (i32, [W, p, p, p, i32, i32, p, i64, i32, i32, p, sz, p, p]),
         "iqk_moe_auto_workspace": (i32, [W, i64, i32, p]),
         "iqk_moe_auto": (i32, [W, p, p, p, i32, i32, p, i64, i32, p, sz, p, p, p]),
+        "iqk_moe_auto_noalloc": (i32, [W, p, p, p, i32, i32, p, i64, i32, p, p, p]),
         "iqk_swiglu": (i32, [p, i64, i64, p, p]),
         "iqk_combine": (i32, [p, p, i64, i32, i64, p, p]),
         "iqk_route": (i32, [p, i64, i64, i32, p, p, p, p]),
@@ -367,6 +368,23 @@ def moe_auto(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=None, grid: 
                              workspace.numel(), _dev(y, "y", torch.float32, T * k * w.out), ctypes.byref(path),
                              _stream(stream)))
     return y, AUTO_PATHS[path.value]
+
+
+def moe_auto_noalloc(w: Weights, x: torch.Tensor, ids: torch.Tensor, y: torch.Tensor, values=None,
+                     grid: torch.Tensor | None = None, x_slots: int = 1, stream=None) -> str:
+    """moe_auto without a workspace and without any allocation: the
+    library's fixed device scratch holds the routing arrays (calls that
+    overlap on one GPU race).  y [T, k, out] float32 is the caller's;
+    returns the path taken."""
+    T, k = ids.shape
+    xp, xdt = _x_args(x, T, x_slots, w.in_features)
+    _v, vp = _host_values(values)
+    cw = w._c()
+    path = ctypes.c_int(-1)
+    _check(_lib.iqk_moe_auto_noalloc(ctypes.byref(cw), vp, _grid(grid), xp, xdt, x_slots, _ids(ids), T, k,
+                                     _dev(y, "y", torch.float32, T * k * w.out), ctypes.byref(path),
+                                     _stream(stream)))
+    return AUTO_PATHS[path.value]
 
 
 def floor_gemv(w: Weights, x: torch.Tensor, ids: torch.Tensor, values=None, grid: torch.Tensor | None = None,

@@ -26,6 +26,7 @@ PER_FILE = {
     "iqk_prefill.hip": [],
     "iqk_fused.hip": [],
     "iqk_glue.hip": [],
+    "iqk_noalloc.hip": [],
     "iqk_host.cpp": [],
     "iqk_relayout.cpp": [],
     "iqk_status.cpp": [],

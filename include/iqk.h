@@ -220,6 +220,21 @@ int iqk_moe_auto(const iqk_weights* w, const float* values, const int8_t* grid,
                  const void* x, int x_dtype, int x_slots, const int32_t* ids, int64_t T, int k,
                  void* workspace, size_t ws_bytes, float* y, int* path, void* stream);
 
+/* iqk_moe_auto for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, hosts that forbid allocation): no
+ * workspace argument; the routing arrays and the work plan live in a fixed
+ * device array of the library (1 MiB on each GPU it runs on, held until
+ * the process ends; its address is taken once per device, on the first
+ * call with that device current).  A call whose
+ * iqk_moe_auto_workspace exceeds 1 MiB returns IQK_E_SIZE (at 256 experts
+ * about 260 k token-expert pairs fit).  The call allocates nothing.  Every
+ * call on one GPU shares that GPU's array and rebuilds its contents, so
+ * calls that overlap on one GPU (different streams, or threads) race.
+ * Arguments, results and errors otherwise as iqk_moe_auto. */
+int iqk_moe_auto_noalloc(const iqk_weights* w, const float* values, const int8_t* grid,
+                         const void* x, int x_dtype, int x_slots, const int32_t* ids, int64_t T, int k,
+                         float* y, int* path, void* stream);
+
 /* The layer steps either side of the projections for the prefill paths
  * (the decode matvec has them as epilogues: iqk_moe_gemv_swiglu,
  * iqk_moe_gemv_combine), with the same arithmetic (SwiGLU of the same
