@@ -317,21 +317,28 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
 
 // plain streaming write (HBM write-ceiling reference): the value in every
 // 16-byte word, non-temporal 16-byte stores, a wave covering 1 KiB per store
-// instruction as the dequantization producer's stores do
-__global__ __launch_bounds__(256) void stream_write_kernel(u32x4* __restrict__ buf, int64_t n16, uint32_t value) {
-    const int64_t stride = (int64_t)gridDim.x * 256;
+// instruction as the dequantization producer's stores do; each workgroup
+// writes one contiguous span of `per_block` words
+__global__ __launch_bounds__(256) void stream_write_kernel(u32x4* __restrict__ buf, int64_t n16, int64_t per_block,
+                                                           uint32_t value) {
+    const int64_t b0 = (int64_t)blockIdx.x * per_block;
+    const int64_t b1 = b0 + per_block < n16 ? b0 + per_block : n16;
     const u32x4 v = {value, value, value, value};
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) __builtin_nontemporal_store(v, buf + i);
+    for (int64_t i = b0 + threadIdx.x; i < b1; i += 256) __builtin_nontemporal_store(v, buf + i);
 }
 
 }  // namespace
 
 hipError_t launch_stream_write(void* buf, size_t bytes, uint32_t value, hipStream_t s) {
     const int64_t n16 = (int64_t)(bytes / 16);
+    // the producer's launch cap; each block's span a whole number of 4 KiB runs
     int64_t blocks = (n16 + 255) / 256;
-    blocks = blocks < 256 * 512 ? blocks : 256 * 512;  // the producer's launch cap
+    blocks = blocks < 256 * 512 ? blocks : 256 * 512;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(stream_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (u32x4*)buf, n16, value);
+    const int64_t per_block = ((n16 + blocks - 1) / blocks + 255) / 256 * 256;
+    blocks = (n16 + per_block - 1) / per_block;
+    hipLaunchKernelGGL(stream_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (u32x4*)buf, n16, per_block,
+                       value);
     return hipGetLastError();
 }
 
