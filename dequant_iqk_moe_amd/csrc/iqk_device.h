@@ -42,17 +42,27 @@ constexpr uint32_t kOob = 0x80000000u;  // an offset past every resource used he
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
+// Cache policy of a buffer load (its aux operand): the default, or the
+// non-temporal hint for data a launch reads once.
+constexpr int kCacheDefault = 0;
+constexpr int kNonTemporal = 2;
+
+template <int AUX = kCacheDefault>
 __device__ __forceinline__ uint4 ld128(Rsrc r, uint32_t off) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
+template <int AUX = kCacheDefault>
 __device__ __forceinline__ uint2 ld64(Rsrc r, uint32_t off) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
     return make_uint2(v[0], v[1]);
 }
-__device__ __forceinline__ uint32_t ld32(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
-__device__ __forceinline__ uint32_t ld16(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0); }
-__device__ __forceinline__ uint32_t ld8(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0); }
+template <int AUX = kCacheDefault>
+__device__ __forceinline__ uint32_t ld32(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX); }
+template <int AUX = kCacheDefault>
+__device__ __forceinline__ uint32_t ld16(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, AUX); }
+template <int AUX = kCacheDefault>
+__device__ __forceinline__ uint32_t ld8(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, AUX); }
 
 // Raw stream words of the 64 weights one lane owns in one row.
 struct RowData {
@@ -102,30 +112,31 @@ __device__ __forceinline__ ExpertRes expert_res(const P& p, int e) {
 }
 
 // The words one lane needs for expert row `row` (rows at or past `out` are
-// out of range and read zeros).  Resources are uniform, offsets per lane.
-template <int FMT, int N>
+// out of range and read zeros).  Resources are uniform, offsets per lane;
+// AUX is the loads' cache policy.
+template <int FMT, int N, int AUX = kCacheDefault>
 __device__ __forceinline__ RowData load_row(const ExpertRes& x, uint32_t row, uint32_t c) {
     using St = Strides<FMT, N>;
     RowData r;
     if constexpr (FMT == IQK_IQ2_K) {
-        r.q = ld128(x.q, row * St::QS + 16u * c);
-        r.a = ld16(x.a, row * St::P1 + 2u * c);
-        r.b = ld8(x.b, row * St::P2 + (c >> 1));
+        r.q = ld128<AUX>(x.q, row * St::QS + 16u * c);
+        r.a = ld16<AUX>(x.a, row * St::P1 + 2u * c);
+        r.b = ld8<AUX>(x.b, row * St::P2 + (c >> 1));
         r.c = 0;
-        r.d = ld16(x.d, row * St::P3 + 2u * (c >> 2));
+        r.d = ld16<AUX>(x.d, row * St::P3 + 2u * (c >> 2));
     } else if constexpr (FMT == IQK_IQ2_KS) {
-        r.q = ld128(x.q, row * St::QS + 16u * c);
-        r.a = ld8(x.a, row * St::P1 + c);
-        r.b = ld8(x.b, row * St::P2 + (c >> 2));
-        r.c = ld8(x.c, row * St::P3 + (c >> 2));
-        r.d = ld16(x.d, row * 2u);
+        r.q = ld128<AUX>(x.q, row * St::QS + 16u * c);
+        r.a = ld8<AUX>(x.a, row * St::P1 + c);
+        r.b = ld8<AUX>(x.b, row * St::P2 + (c >> 2));
+        r.c = ld8<AUX>(x.c, row * St::P3 + (c >> 2));
+        r.d = ld16<AUX>(x.d, row * 2u);
     } else {
-        const uint2 qq = ld64(x.q, row * St::QS + 8u * c);
+        const uint2 qq = ld64<AUX>(x.q, row * St::QS + 8u * c);
         r.q = make_uint4(qq.x, qq.y, 0, 0);
-        r.a = ld32(x.a, row * St::P1 + 4u * c);
+        r.a = ld32<AUX>(x.a, row * St::P1 + 4u * c);
         r.b = 0;
         r.c = 0;
-        r.d = ld16(x.d, row * 2u);
+        r.d = ld16<AUX>(x.d, row * 2u);
     }
     return r;
 }

@@ -432,13 +432,19 @@ struct Group {
 };
 
 // Rows of one unit: local row q = it * RPI + lane_row maps to an expert row
-// through `row_of` (identity plus offset, or the gate/up split).
+// through `row_of` (identity plus offset, or the gate/up split).  A launch
+// reads each row once, so the loads carry the non-temporal hint: measured on
+// one-token launches, 10.5 -> 9.7 us (IQ2_K gate/up) and 7.0 -> 6.1 us
+// (down), the floor variant likewise, while the small data every launch
+// re-reads (activation, ids, grid) is no longer pushed out of the L2 by the
+// streamed rows.  (The fused prefill, whose tiles share rows through the L2,
+// is slower with it and keeps the default.)
 template <int FMT, int N, class RowOf>
 __device__ __forceinline__ void load_group(Group<FMT, N>& g, const ExpertRes& res, RowOf row_of, int lane_row, int c) {
     using G = Geo<N>;
 #pragma unroll
     for (int it = 0; it < G::GIT; ++it)
-        g.r[it] = load_row<FMT, N>(res, (uint32_t)row_of(it * G::RPI + lane_row), (uint32_t)c);
+        g.r[it] = load_row<FMT, N, kNonTemporal>(res, (uint32_t)row_of(it * G::RPI + lane_row), (uint32_t)c);
 }
 
 // float -> bf16, round to nearest even (NaN stays a quiet NaN)
