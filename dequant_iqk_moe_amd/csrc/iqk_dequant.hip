@@ -224,9 +224,19 @@ template <int OUT_DT>
 struct WideShape {
     static constexpr int ESZ = OUT_DT == IQK_F32 ? 4 : 2;
     static constexpr int CB = kWideChunk * ESZ;       // output bytes per lane
-    static constexpr int PITCH = CB + 16;              // LDS pitch per lane (bank spread)
+    static constexpr int SLOTS = CB / 16;              // 16-byte slots per lane
     static constexpr int WORDS = CB / 4;
 };
+
+// Byte offset of 16-byte slot i of lane `lane`'s run in the stage: the runs
+// sit back to back (no padding) and each lane's slots are rotated by an XOR
+// with its lane index, so eight lanes writing the same slot, and eight lanes
+// reading one run, touch distinct banks.
+template <int OUT_DT>
+__device__ __forceinline__ int stage_off(int lane, int i) {
+    using WS = WideShape<OUT_DT>;
+    return lane * WS::CB + 16 * (i ^ (lane & (WS::SLOTS - 1)));
+}
 
 template <int OUT_DT>
 __device__ __forceinline__ uint32_t cvt_pair(float a, float b) {
@@ -242,7 +252,7 @@ __device__ __forceinline__ uint32_t cvt_pair(float a, float b) {
 // Decode one 64-weight chunk into output words (f32: 64 words, f16/bf16: 32).
 template <int FMT, int OUT_DT, bool FLOOR>
 __device__ __forceinline__ void decode_chunk(const DequantParams& p, int64_t row, int64_t c, const float* tab,
-                                             const uint2* grid_s, uint32_t* o) {
+                                             const uint2* grid_s, const uint16_t* grid_p, uint32_t* o) {
     const uint8_t* S = p.streams;
     const int64_t n = p.n;
     float w[kWideChunk];
@@ -321,8 +331,11 @@ __device__ __forceinline__ void decode_chunk(const DequantParams& p, int64_t row
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const uint32_t idx = ((qsw >> (8 * j)) & 0xFFu) | (((h16 >> (3 * j)) & 7u) << 8);
-                    const uint2 gv = grid_s[idx];
-                    const uint32_t vx = gv.x & 0x03030303u, vy = gv.y & 0x03030303u;
+                    // the packed entry: nibble k holds the codes of values k
+                    // and k + 4; one v_perm_b32 spreads the nibbles to bytes
+                    const uint32_t e = grid_p[idx];
+                    const uint32_t wv = __builtin_amdgcn_perm(e >> 4, e, 0x05010400u);
+                    const uint32_t vx = wv & 0x03030303u, vy = (wv >> 2) & 0x03030303u;
                     const uint32_t vx4 = vx | 0x04040404u, vy4 = vy | 0x04040404u;
                     // selectors [c_a, 4 + c_a, c_b, 4 + c_b] for the pairs (0, 1) and (2, 3)
                     o[16 * b + 4 * j + 0] = __builtin_amdgcn_perm(thi, tlo, __builtin_amdgcn_perm(vx4, vx, 0x05010400u));
@@ -364,30 +377,46 @@ __device__ __forceinline__ void decode_chunk(const DequantParams& p, int64_t row
     }
 }
 
+// Low two bits of each value's byte packed into a 16-bit grid entry: nibble
+// k = code(value k) | code(value k + 4) << 2, for the two words w of an
+// entry (values 0-3 in w0, 4-7 in w1).
+__device__ __forceinline__ uint32_t pack_codes(uint32_t w0, uint32_t w1) {
+    const uint32_t nib = (w0 & 0x03030303u) | ((w1 & 0x03030303u) << 2);  // byte k: nibble k
+    return (nib & 0xFu) | ((nib >> 4) & 0xF0u) | ((nib >> 8) & 0xF00u) | ((nib >> 12) & 0xF000u);
+}
+
 template <int FMT, int OUT_DT, bool FLOOR>
 __global__ __launch_bounds__(kThreads) void dequant_wide_kernel(DequantParams p) {
     using WS = WideShape<OUT_DT>;
-    __shared__ float tab[8];
-    __shared__ uint2 grid_s[FMT == IQK_IQ1_S_R4 ? 2048 : 1];
-    __shared__ __attribute__((aligned(16))) uint8_t stage[kThreads * WS::PITCH];
+    // f16 / bf16 output of IQ1_S_R4 looks each weight up among the three
+    // values a ternary grid gives, so its LDS copy of the grid keeps only
+    // each value's two low bits (4 KiB: with the 32 KiB stage, four
+    // workgroups fit a CU's LDS); a grid holding any other value makes the
+    // whole output NaN (checked while the grid is staged).  The float32
+    // output takes any int8 value and stages the whole grid.
+    constexpr bool kTernary = FMT == IQK_IQ1_S_R4 && OUT_DT != IQK_F32 && !FLOOR;
+    constexpr bool kWholeGrid = FMT == IQK_IQ1_S_R4 && OUT_DT == IQK_F32 && !FLOOR;
+    __shared__ float tab[FMT == IQK_IQ1_S_R4 ? 1 : 8];
+    __shared__ uint2 grid_s[kWholeGrid ? 2048 : 1];
+    __shared__ uint16_t grid_p[kTernary ? 2048 : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kThreads * WS::CB];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    if (tid < 8) tab[tid] = p.values[tid];
-    // f16 / bf16 output of IQ1_S_R4 looks each weight up among the three
-    // values a ternary grid gives; a grid holding any other value makes the
-    // whole output NaN (checked while the grid is staged)
-    constexpr bool kTernary = FMT == IQK_IQ1_S_R4 && OUT_DT != IQK_F32 && !FLOOR;
+    if constexpr (FMT != IQK_IQ1_S_R4) {
+        if (tid < 8) tab[tid] = p.values[tid];
+    }
     uint32_t off_grid = 0;
-    if constexpr (FMT == IQK_IQ1_S_R4) {
-        if (!FLOOR) {
-            const uint4* src = (const uint4*)p.grid;
-            uint4* dst = (uint4*)grid_s;
-            for (int i = tid; i < 1024; i += kThreads) {
-                const uint4 v = src[i];
-                dst[i] = v;
-                if constexpr (kTernary) off_grid |= non_ternary(v.x) | non_ternary(v.y) | non_ternary(v.z) | non_ternary(v.w);
-            }
+    if constexpr (kWholeGrid) {
+        const uint4* src = (const uint4*)p.grid;
+        uint4* dst = (uint4*)grid_s;
+        for (int i = tid; i < 1024; i += kThreads) dst[i] = src[i];
+    } else if constexpr (kTernary) {
+        const uint4* src = (const uint4*)p.grid;  // two entries per 16 bytes
+        for (int i = tid; i < 1024; i += kThreads) {
+            const uint4 v = src[i];
+            off_grid |= non_ternary(v.x) | non_ternary(v.y) | non_ternary(v.z) | non_ternary(v.w);
+            *(uint32_t*)&grid_p[2 * i] = pack_codes(v.x, v.y) | (pack_codes(v.z, v.w) << 16);
         }
     }
     const bool nan_out = kTernary ? __syncthreads_or(off_grid != 0) != 0 : (__syncthreads(), false);
@@ -395,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void dequant_wide_kernel(DequantParams p)
     const int64_t cpr = p.ipr;                 // chunks per row
     const int64_t chunks = p.nrows * cpr;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    uint8_t* my = stage + tid * WS::PITCH;
+    uint8_t* wst = stage + wave * 64 * WS::CB;  // the wave's runs
     const int64_t total_bytes = chunks * WS::CB;
     int64_t ch = (int64_t)blockIdx.x * kThreads + tid;
     int64_t lr = ch / cpr;
@@ -408,27 +437,27 @@ __global__ __launch_bounds__(kThreads) void dequant_wide_kernel(DequantParams p)
         }
         if (ch < chunks) {
             uint32_t o[WS::WORDS];
-            decode_chunk<FMT, OUT_DT, FLOOR>(p, p.row0 + lr, col, tab, grid_s, o);
+            decode_chunk<FMT, OUT_DT, FLOOR>(p, p.row0 + lr, col, tab, grid_s, grid_p, o);
             if (kTernary && nan_out) {
 #pragma unroll
                 for (int i = 0; i < WS::WORDS; ++i) o[i] = OUT_DT == IQK_F16 ? 0x7E007E00u : 0x7FC07FC0u;
             }
 #pragma unroll
-            for (int i = 0; i < WS::WORDS / 4; ++i) *(uint4*)(my + 16 * i) = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+            for (int i = 0; i < WS::SLOTS; ++i)
+                *(uint4*)(wst + stage_off<OUT_DT>(lane, i)) = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
         }
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // the wave's 64 chunks are contiguous in the output: store 1 KiB runs
         const int64_t out0 = base * WS::CB;
-        const uint8_t* wst = stage + wave * 64 * WS::PITCH;
 #pragma unroll
         for (int s2 = 0; s2 < WS::CB / 16; ++s2) {
             const int o = s2 * 1024 + 16 * lane;          // byte offset within the wave's output run
             const int src_lane = o / WS::CB, within = o % WS::CB;
             const int64_t ob = out0 + o;
             if (ob < total_bytes) {
-                const uint4 v = *(const uint4*)(wst + src_lane * WS::PITCH + within);
+                const uint4 v = *(const uint4*)(wst + stage_off<OUT_DT>(src_lane, within / 16));
                 u32x4 vv = {v.x, v.y, v.z, v.w};
                 __builtin_nontemporal_store(vv, (u32x4*)((uint8_t*)p.out + ob));
             }
