@@ -326,19 +326,32 @@ __device__ __forceinline__ int dot4_first(uint32_t a, uint32_t b) {
 // hand-placed v_bitop3_b32).
 __device__ __forceinline__ uint32_t and_or_fast(uint32_t a, uint32_t b, uint32_t c) { return (a & b) | c; }
 
-// 16 weights of one code word against 4 activation words, as one chain.
+// int8 weights of two code words (16 each) from the value table: word i,
+// byte b of w[i][jj] holds weight 4 b + jj, alphabet bits m[i] (0 or 4 in
+// every byte).  The codes of a shift step come from one 64-bit shift of the
+// word pair (v_lshrrev_b64 moves both words; the bits crossing from the
+// high word into the low one land above each byte's two code bits, which
+// the mask drops): 3 shifts per 32 weights instead of 6.
+__device__ __forceinline__ void expand_pair(uint32_t q0, uint32_t q1, uint32_t m0, uint32_t m1, uint32_t tlo,
+                                            uint32_t thi, uint32_t (&w0)[4], uint32_t (&w1)[4]) {
+    const uint64_t qq = ((uint64_t)q1 << 32) | q0;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        uint64_t sh = qq;
+        if (jj > 0) asm("v_lshrrev_b64 %0, %1, %2" : "=v"(sh) : "i"(2 * jj), "v"(qq));
+        w0[jj] = __builtin_amdgcn_perm(thi, tlo, and_or_fast((uint32_t)sh, 0x03030303u, m0));
+        w1[jj] = __builtin_amdgcn_perm(thi, tlo, and_or_fast((uint32_t)(sh >> 32), 0x03030303u, m1));
+    }
+}
+
+// 16 weights (4 words) against 4 activation words, as one chain.
 template <bool FIRST>
-__device__ __forceinline__ int dot16(uint32_t qw, uint32_t m, uint32_t tlo, uint32_t thi, const uint32_t* x4, int acc) {
-    const uint32_t M = 0x03030303u;
-    const uint32_t w0 = __builtin_amdgcn_perm(thi, tlo, and_or_fast(qw, M, m));
-    const uint32_t w1 = __builtin_amdgcn_perm(thi, tlo, and_or_fast(qw >> 2, M, m));
-    const uint32_t w2 = __builtin_amdgcn_perm(thi, tlo, and_or_fast(qw >> 4, M, m));
-    const uint32_t w3 = __builtin_amdgcn_perm(thi, tlo, and_or_fast(qw >> 6, M, m));
-    if constexpr (FIRST) acc = dot4_first(w0, x4[0]);
-    else acc = __builtin_amdgcn_sdot4((int)w0, (int)x4[0], acc, false);
-    acc = __builtin_amdgcn_sdot4((int)w1, (int)x4[1], acc, false);
-    acc = __builtin_amdgcn_sdot4((int)w2, (int)x4[2], acc, false);
-    acc = __builtin_amdgcn_sdot4((int)w3, (int)x4[3], acc, false);
+__device__ __forceinline__ int dot16w(const uint32_t (&w)[4], const uint32_t* x4, int acc) {
+    if constexpr (FIRST) acc = dot4_first(w[0], x4[0]);
+    else acc = __builtin_amdgcn_sdot4((int)w[0], (int)x4[0], acc, false);
+    acc = __builtin_amdgcn_sdot4((int)w[1], (int)x4[1], acc, false);
+    acc = __builtin_amdgcn_sdot4((int)w[2], (int)x4[2], acc, false);
+    acc = __builtin_amdgcn_sdot4((int)w[3], (int)x4[3], acc, false);
     return acc;
 }
 
@@ -354,13 +367,11 @@ __device__ __forceinline__ float row_dot(const RowData& r, int c, const uint32_t
         // all four sub-blocks' weights first, then eight interleaved dot
         // chains (hi/lo x 4 sub-blocks), so dependent ops are not adjacent
         uint32_t w[4][4];
+        uint32_t m[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)sx, i, 1) & 0x04040404u;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                w[i][jj] = __builtin_amdgcn_perm(thi, tlo, and_or_fast(q[i] >> (2 * jj), 0x03030303u, m));
-        }
+        for (int i = 0; i < 4; ++i) m[i] = (uint32_t)__builtin_amdgcn_sbfe((int)sx, i, 1) & 0x04040404u;
+        expand_pair(q[0], q[1], m[0], m[1], tlo, thi, w[0], w[1]);
+        expand_pair(q[2], q[3], m[2], m[3], tlo, thi, w[2], w[3]);
         int h[4], l[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -392,10 +403,12 @@ __device__ __forceinline__ float row_dot(const RowData& r, int c, const uint32_t
             const uint32_t raw = ((r.a >> (4 * s)) & 15u) | (((schx >> (sh + s)) & 1u) << 4);
             const int si = __builtin_amdgcn_sbfe((int)raw, 0, 5);
             const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)r.c, sh + s, 1) & 0x04040404u;
-            int h = dot16<true>(q[2 * s], m, tlo, thi, xh + 8 * s, 0);
-            h = dot16<false>(q[2 * s + 1], m, tlo, thi, xh + 8 * s + 4, h);
-            int l = dot16<true>(q[2 * s], m, tlo, thi, xl + 8 * s, 0);
-            l = dot16<false>(q[2 * s + 1], m, tlo, thi, xl + 8 * s + 4, l);
+            uint32_t w0[4], w1[4];
+            expand_pair(q[2 * s], q[2 * s + 1], m, m, tlo, thi, w0, w1);
+            int h = dot16w<true>(w0, xh + 8 * s, 0);
+            h = dot16w<false>(w1, xh + 8 * s + 4, h);
+            int l = dot16w<true>(w0, xl + 8 * s, 0);
+            l = dot16w<false>(w1, xl + 8 * s + 4, l);
             ah += __mul24(h, si);
             al += __mul24(l, si);
         }
