@@ -148,8 +148,12 @@ def timed_graph(torch, fn, S, reps, warm_reps, ramp=True, info=None):
         g.replay()
     torch.cuda.synchronize()
     ramp_calls = ramp_clocks(torch, g.replay) if ramp else 0
+    # one more untimed replay, not waited for: the GPU is busy with it while
+    # the start event and the timed replays are queued, so the idle GPU's
+    # wake-up and the first launch's latency stay out of the timed region
+    g.replay()
     if info is not None:
-        info["untimed_replays"] = warm_reps + ramp_calls
+        info["untimed_replays"] = warm_reps + ramp_calls + 1
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
