@@ -470,18 +470,39 @@ GEMV_SOURCES = ("dequant_iqk_moe_amd/csrc/iqk_gemv.hip", "dequant_iqk_moe_amd/cs
                 "dequant_iqk_moe_amd/csrc/iqk_internal.h")
 
 
-def measured_traffic():
-    """HBM bytes per gate/up launch from the committed FETCH_SIZE/WRITE_SIZE
-    summary, or None when the kernel sources changed since it was taken."""
+def _traffic_fields():
+    """the committed FETCH_SIZE/WRITE_SIZE summary's fields, or None when the
+    matvec sources changed since the counters were taken"""
     try:
         text = open(TRAFFIC_PROFILE).read()
     except OSError:
         return None
     fields = dict(line.split(": ", 1) for line in text.splitlines()
-                  if line.startswith(("traffic_bytes_per_launch: ", "source_sha256: ")))
+                  if line.startswith(("traffic_bytes_per_launch: ", "floor_fetch_bytes_per_launch: ",
+                                      "algorithmic_bytes_per_launch: ", "source_sha256: ")))
     if fields.get("source_sha256", "").strip() != gemv_source_hash():
         return None
-    return int(fields["traffic_bytes_per_launch"])
+    return fields
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed counter summary, or
+    None when the kernel sources changed since it was taken."""
+    f = _traffic_fields()
+    return int(f["traffic_bytes_per_launch"]) if f else None
+
+
+def deleted_load_check():
+    """The pages' third pricing gate ("Pricing": no deleted-load signature):
+    the floor arm must read what the decode reads.  From the same counter
+    summary: the floor kernel's scaled FETCH_SIZE over the algorithmic bytes,
+    ok at >= 0.98; None when the summary does not match the sources."""
+    f = _traffic_fields()
+    if not f or "floor_fetch_bytes_per_launch" not in f:
+        return None
+    ratio = int(f["floor_fetch_bytes_per_launch"]) / int(f["algorithmic_bytes_per_launch"])
+    return {"floor_fetch_over_algorithmic": round(ratio, 4), "ok": ratio >= 0.98,
+            "source": os.path.relpath(TRAFFIC_PROFILE, ROOT)}
 
 
 def gemv_source_hash():
@@ -925,6 +946,7 @@ def main():
                           "clock_ramp_s": CLOCK_RAMP_S, "untimed_steps_run": head_info["untimed_replays"] * S},
         "cells_passing_ratio_bar": _count(cells, "ratio_ok"),
         "cells_passing_floor_band": _count(cells, "band_ok"),
+        "deleted_load_check": deleted_load_check(),
         "cells": cells,
         "cpu_baseline": cpu,
     }

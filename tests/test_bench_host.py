@@ -3,7 +3,8 @@
 * a multi-GPU request exits before touching any device, with a message;
 * the kernel-source fingerprint that keys the recorded HBM traffic ignores
   comments and whitespace but not code;
-* the recorded traffic is reported only while the fingerprint matches.
+* the recorded traffic, and the deleted-load gate read from the same counter
+  summary, are reported only while the fingerprint matches.
 """
 import json
 import os
@@ -54,3 +55,22 @@ def test_traffic_reported_only_for_matching_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic() is None
     monkeypatch.setattr(bench, "TRAFFIC_PROFILE", str(tmp_path / "absent.md"))
     assert bench.measured_traffic() is None
+
+
+def test_deleted_load_check_from_the_counter_summary(tmp_path, monkeypatch):
+    prof = tmp_path / "traffic.md"
+    h = bench.gemv_source_hash()
+    monkeypatch.setattr(bench, "TRAFFIC_PROFILE", str(prof))
+    prof.write_text("traffic_bytes_per_launch: 1010\nfloor_fetch_bytes_per_launch: 990\n"
+                    "algorithmic_bytes_per_launch: 1000\nsource_sha256: %s\n" % h)
+    chk = bench.deleted_load_check()
+    assert chk["floor_fetch_over_algorithmic"] == 0.99 and chk["ok"]
+    # a floor that reads less than 98 % of the algorithmic bytes skipped loads
+    prof.write_text("traffic_bytes_per_launch: 1010\nfloor_fetch_bytes_per_launch: 970\n"
+                    "algorithmic_bytes_per_launch: 1000\nsource_sha256: %s\n" % h)
+    assert not bench.deleted_load_check()["ok"]
+    # stale summary: no verdict
+    prof.write_text("traffic_bytes_per_launch: 1010\nfloor_fetch_bytes_per_launch: 990\n"
+                    "algorithmic_bytes_per_launch: 1000\nsource_sha256: %s\n" % ("0" * 64))
+    assert bench.deleted_load_check() is None
+
