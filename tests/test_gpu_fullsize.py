@@ -12,6 +12,9 @@ oracle is float32 summation order) and <= 2e-2 against the float32
 weights; the producer's bf16 rows bit-exact.  Vectors: all six pairs of a
 one-token call, eight whole pairs of every larger call.
 
+The one-token layer's glue modes (SwiGLU epilogue, router-weighted
+combine) get the same whole-vector comparison on the full IQ2_K tensors.
+
 Inputs: `synth.wire_experts` (one drawn expert, every other expert a copy
 with its non-scale bytes XORed by a byte of its own), so the full stacked
 tensors are built in seconds while every expert differs."""
@@ -24,7 +27,7 @@ import torch
 import oracle
 import synth
 import dequant_iqk_moe_amd as q
-from gpu_common import TOL_BF16, TOL_GEMV, announce, rel_err_per_vector, to_dev
+from gpu_common import TOL_BF16, TOL_GEMV, announce, bf16_storage_excess, rel_err_per_vector, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -130,4 +133,41 @@ def test_fullsize(fmt, proj):
         got = dense[e * F.out + r].cpu().view(torch.int16).numpy().view(np.uint16)
         assert np.array_equal(got, F.row(e, r, oracle.BF16))
     del dense, F
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_layer_glue_modes():
+    """The one-token layer the benchmark times, on the full stacked IQ2_K
+    tensors: gate/up with the SwiGLU epilogue (every pair's whole h vector
+    at the SwiGLU bar: the matvec's 1e-3 past the bf16 cast's half step),
+    then down with the router-weighted combine on that h (the token's whole
+    y vector at 1e-3 of sum_j |w_j| ||W_j h_j||); T = 1 and 4."""
+    announce("full-size layer glue: building the stacked IQ2_K weights")
+    Fg = Full(K, "gate_up", 3400)
+    Fd = Full(K, "down", 3405)
+    I = Fd.n
+    for T in (1, 4):
+        announce(f"full-size layer glue T={T}")
+        x, ids = _inputs(Fg, T, 3500 + T)
+        rw = np.random.default_rng(3600 + T).dirichlet(np.ones(TOPK), size=T).astype(np.float32)
+        idd = to_dev(ids)
+        h = q.moe_gemv_swiglu(Fg.w, x.cuda(), idd, Fg.values)
+        # the combine takes this h; down's value table is its own (as the bench's layer)
+        y = q.moe_gemv_combine(Fd.w, h, idd, to_dev(rw), Fd.values, x_slots=TOPK)
+        hv = h.float().cpu().numpy()
+        yv = y.cpu().numpy()
+        xv = x.float().numpy()
+        for t in range(T):
+            for e in (int(v) for v in ids[t]):
+                Fg.expert_streams(e)
+                Fd.expert_streams(e)
+            gu = list(_POOL.map(lambda j: Fg.vector(int(ids[t, j]), xv[t, 0]), range(TOPK)))
+            h_ref = oracle.swiglu(np.stack(gu)[None])[0]                      # [k, I]
+            assert np.all(bf16_storage_excess(hv[t], h_ref) <= TOL_GEMV)
+            parts = np.stack(list(_POOL.map(lambda j: Fd.vector(int(ids[t, j]), hv[t, j]), range(TOPK))))
+            y_ref = oracle.combine(parts[None], rw[t:t + 1])[0]
+            scale = np.sum(np.abs(rw[t])[:, None] * np.linalg.norm(parts, axis=-1, keepdims=True))
+            assert np.linalg.norm(yv[t] - y_ref) / scale <= TOL_GEMV
+        assert h.shape == (T, TOPK, I)
+    del Fg, Fd
     torch.cuda.empty_cache()
