@@ -615,7 +615,7 @@ def _count(cells, key):
 
 def oracle_threads():
     """host threads for the all-core oracle run: the CPUs this process may
-    use, at most 16 (a GPU machine's CPU share)"""
+    use, at most 16 (the CPU share of one GPU on the target hosts)"""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
