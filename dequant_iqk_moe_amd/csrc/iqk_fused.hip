@@ -24,8 +24,11 @@
 //     the lane builds a 4-entry bf16 table of its possible weights
 //     (scale * table value, or scale * (grid value + shift)); each bf16 pair
 //     of a fragment is then one v_perm_b32 of that table, its selector one
-//     v_perm_b32 of doubled code bytes.  About 2-3 VALU instructions per
-//     weight, once per weight whatever the number of tokens.
+//     v_perm_b32 of code bytes (2-bit members: the table as two packed bf16
+//     pairs and selector bytes 2c, 2c + 1; IQ1_S_R4, whose codes come from
+//     grid bytes: the table split into low and high bytes and selector bytes
+//     c, 4 + c).  About 2-3 VALU instructions per weight, once per weight
+//     whatever the number of tokens.
 //   * The expert's token rows (gathered through the routing permutation)
 //     are staged in LDS (all of k for up to 16 tokens, 2048 k at a time for
 //     up to 32), already in
@@ -108,6 +111,20 @@ __device__ __forceinline__ uint32_t table_pair(const Tab& t, uint32_t v, uint32_
     return __builtin_amdgcn_perm(t.hi, t.lo, __builtin_amdgcn_perm(v4, v, sel));
 }
 
+// A 4-entry bf16 table kept as two packed pairs (value c at bytes 2c and
+// 2c + 1 of the 8 bytes {p23, p01}): a pair of weights with codes (a, b) is
+// perm(p23, p01, [2a, 2a + 1, 2b, 2b + 1]), its selector one perm of the
+// doubled codes v2 and v2 + 1 -- no byte split of the table is needed.
+struct PairTab {
+    uint32_t p01, p23;
+};
+__device__ __forceinline__ PairTab make_pair_tab(float v0, float v1, float v2, float v3) {
+    return PairTab{pk_bf16(v0, v1), pk_bf16(v2, v3)};
+}
+__device__ __forceinline__ uint32_t pair_lookup(const PairTab& t, uint32_t v2, uint32_t v2p, uint32_t sel) {
+    return __builtin_amdgcn_perm(t.p23, t.p01, __builtin_amdgcn_perm(v2p, v2, sel));
+}
+
 // The value table in vector registers, as named members: an array here
 // would be turned into a private-memory lookup by the alphabet select.
 struct Table8 {
@@ -125,7 +142,7 @@ __device__ __forceinline__ void decode_chunk(const RowData& r, int c, const Tabl
     const float d = half_to_float(r.d);
     if constexpr (FMT == IQK_IQ2_K || FMT == IQK_IQ2_KS) {
         const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
-        Tab t{0u, 0u};
+        PairTab t{0u, 0u};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (FMT == IQK_IQ2_K || (i & 1) == 0) {  // IQ2_KS: one table per two code words
@@ -149,17 +166,17 @@ __device__ __forceinline__ void decode_chunk(const RowData& r, int c, const Tabl
                     asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(hi), "v"(lo));
                     return r;
                 };
-                t = make_tab(s * pick(tv.v0, tv.v4), s * pick(tv.v1, tv.v5), s * pick(tv.v2, tv.v6),
+                t = make_pair_tab(s * pick(tv.v0, tv.v4), s * pick(tv.v1, tv.v5), s * pick(tv.v2, tv.v6),
                              s * pick(tv.v3, tv.v7));
             }
             u32x4 f0, f1;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                // bytes of v: codes of weights jj, 4 + jj, 8 + jj, 12 + jj
-                const uint32_t v = (q[i] >> (2 * jj)) & 0x03030303u;
-                const uint32_t v4 = v + 0x04040404u;
-                f0[jj] = table_pair(t, v, v4, sel_pair(0, 2));  // (jj, 8 + jj)
-                f1[jj] = table_pair(t, v, v4, sel_pair(1, 3));  // (4 + jj, 12 + jj)
+                // bytes of v2: twice the codes of weights jj, 4 + jj, 8 + jj, 12 + jj
+                const uint32_t v2 = (jj == 0 ? q[i] << 1 : q[i] >> (2 * jj - 1)) & 0x06060606u;
+                const uint32_t v2p = v2 | 0x01010101u;
+                f0[jj] = pair_lookup(t, v2, v2p, sel_pair(0, 2));  // (jj, 8 + jj)
+                f1[jj] = pair_lookup(t, v2, v2p, sel_pair(1, 3));  // (4 + jj, 12 + jj)
             }
             emit(2 * i, f0);
             emit(2 * i + 1, f1);
