@@ -417,7 +417,7 @@ __device__ __forceinline__ uint32_t pack_codes(uint32_t w0, uint32_t w1) {
     return (nib & 0xFu) | ((nib >> 4) & 0xF0u) | ((nib >> 8) & 0xF00u) | ((nib >> 12) & 0xF000u);
 }
 
-template <int FMT, int OUT_DT, bool FLOOR>
+template <int FMT, int OUT_DT, bool FLOOR, bool AHEAD>
 __global__ __launch_bounds__(kThreads) void dequant_wide_kernel(DequantParams p) {
     using WS = WideShape<OUT_DT>;
     // f16 / bf16 output of IQ1_S_R4 looks each weight up among the three
@@ -461,15 +461,12 @@ __global__ __launch_bounds__(kThreads) void dequant_wide_kernel(DequantParams p)
     int64_t ch = (int64_t)blockIdx.x * kThreads + tid;
     int64_t lr = ch / cpr;
     int64_t col = ch - lr * cpr;
-    // IQ1_S_R4: each lane requests its next chunk's words before decoding
-    // the current one, so their latency runs under the grid lookups, the
-    // decode and the stores (the compiler keeps loads behind earlier stores
-    // to the output, which it cannot prove disjoint from the streams).
-    // Measured (bf16 out, 256 experts): gate/up 1800 -> 1628 us, down 870 ->
-    // 796 us.  The 2-bit members load each chunk's words just before decoding
-    // it: ahead, their 4096-wide rows were 1-6 % slower (2048-wide rows 2-5 %
-    // faster, but a width-dependent choice cost the 2048-wide IQ2_KS rows 2 %).
-    constexpr bool ahead = FMT == IQK_IQ1_S_R4;
+    // AHEAD: each lane requests its next chunk's words before decoding the
+    // current one, so their latency runs under the decode and the stores (the
+    // compiler keeps loads behind earlier stores to the output, which it
+    // cannot prove disjoint from the streams).  Otherwise each chunk's words
+    // are loaded just before it is decoded.
+    constexpr bool ahead = AHEAD;
     ChunkWords cur{};
     if (ahead && ch < chunks) cur = load_chunk<FMT>(p, p.row0 + lr, col);
     for (int64_t base = (int64_t)blockIdx.x * kThreads + wave * 64; base < chunks;
@@ -525,6 +522,12 @@ __global__ __launch_bounds__(kThreads) void dequant_wide_kernel(DequantParams p)
 
 template <int FMT, int OUT_DT, bool FLOOR>
 hipError_t launch_wide(DequantParams p, hipStream_t s) {
+    // loads one chunk ahead for IQ1_S_R4 (its grid lookups lengthen every
+    // chunk's dependency chain) and for rows of at most 2048 weights.
+    // Measured (bf16 out, 256 experts): IQ1_S_R4 gate/up 1800 -> 1626 us,
+    // down 867 -> 793 us; IQ2_K down 858 -> 818 us, IQ2_KS down 808 -> 789
+    // us; the 2-bit members' 4096-wide rows were 1-6 % slower ahead.
+    const bool ahead = FMT == IQK_IQ1_S_R4 || p.n <= 2048;
     p.ipr = p.n / kWideChunk;
     const int64_t chunks = p.nrows * p.ipr;
     constexpr int64_t kPerThread = FMT == IQK_IQ1_S_R4 && !FLOOR ? IQK_DEQUANT_GRID_CHUNKS : 1;
@@ -534,7 +537,12 @@ hipError_t launch_wide(DequantParams p, hipStream_t s) {
     const int64_t stride = blocks * kThreads;
     p.step_row = stride / p.ipr;
     p.step_col = stride % p.ipr;
-    hipLaunchKernelGGL((dequant_wide_kernel<FMT, OUT_DT, FLOOR>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+    if (ahead)
+        hipLaunchKernelGGL((dequant_wide_kernel<FMT, OUT_DT, FLOOR, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                           s, p);
+    else
+        hipLaunchKernelGGL((dequant_wide_kernel<FMT, OUT_DT, FLOOR, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                           s, p);
     return hipGetLastError();
 }
 
