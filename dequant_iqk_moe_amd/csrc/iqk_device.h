@@ -84,6 +84,8 @@ struct Strides {
 // its loads read zeros and move no data.
 struct ExpertRes {
     Rsrc q, a, b, c, d;
+    const uint8_t* dp;  // the expert's per-row scale plane (expert 0's for an invalid id)
+    uint32_t dmax;      // its last row (reads of later rows are clamped to it)
 };
 
 template <int FMT, int N, class P>
@@ -94,6 +96,7 @@ __device__ __forceinline__ ExpertRes expert_res(const P& p, int e) {
     const uint32_t rows = valid ? (uint32_t)p.out : 0u;
     const uint8_t* S = p.S;
     ExpertRes r;
+    r.dmax = (uint32_t)p.out - 1u;
     r.q = make_rsrc(S + p.off0 + row0 * St::QS, rows * St::QS);
     r.a = make_rsrc(S + p.off1 + row0 * St::P1, rows * St::P1);
     if constexpr (FMT == IQK_IQ2_K) {
@@ -104,17 +107,31 @@ __device__ __forceinline__ ExpertRes expert_res(const P& p, int e) {
         r.b = make_rsrc(S + p.off2 + row0 * St::P2, rows * St::P2);
         r.c = make_rsrc(S + p.off3 + row0 * St::P3, rows * St::P3);
         r.d = make_rsrc(S + p.off4 + row0 * 2, rows * 2u);
+        r.dp = S + p.off4 + row0 * 2;
     } else {
         r.d = make_rsrc(S + p.off2 + row0 * 2, rows * 2u);
+        r.dp = S + p.off2 + row0 * 2;
         r.b = r.c = r.d;
     }
     return r;
 }
 
+// 16-bit word at a wave-uniform address, through the scalar data cache (the
+// constant address space makes it a scalar load).  The load takes the aligned
+// 32-bit word holding it: that word lies in the same page as the 16-bit word,
+// so it stays in mapped memory even at the end of a buffer.
+__device__ __forceinline__ uint32_t sload_u16(const uint8_t* p) {
+    const uintptr_t a = (uintptr_t)p;
+    const __attribute__((address_space(4))) uint32_t* cp =
+        (const __attribute__((address_space(4))) uint32_t*)(a & ~(uintptr_t)3);
+    const uint32_t w = *cp;
+    return (a & 2u) ? (w >> 16) : (w & 0xFFFFu);
+}
+
 // The words one lane needs for expert row `row` (rows at or past `out` are
 // out of range and read zeros).  Resources are uniform, offsets per lane;
 // AUX is the loads' cache policy.
-template <int FMT, int N, int AUX = kCacheDefault>
+template <int FMT, int N, int AUX = kCacheDefault, bool NO_D = false>
 __device__ __forceinline__ RowData load_row(const ExpertRes& x, uint32_t row, uint32_t c) {
     using St = Strides<FMT, N>;
     RowData r;
@@ -129,14 +146,14 @@ __device__ __forceinline__ RowData load_row(const ExpertRes& x, uint32_t row, ui
         r.a = ld8<AUX>(x.a, row * St::P1 + c);
         r.b = ld8<AUX>(x.b, row * St::P2 + (c >> 2));
         r.c = ld8<AUX>(x.c, row * St::P3 + (c >> 2));
-        r.d = ld16<AUX>(x.d, row * 2u);
+        r.d = NO_D ? 0u : ld16<AUX>(x.d, row * 2u);
     } else {
         const uint2 qq = ld64<AUX>(x.q, row * St::QS + 8u * c);
         r.q = make_uint4(qq.x, qq.y, 0, 0);
         r.a = ld32<AUX>(x.a, row * St::P1 + 4u * c);
         r.b = 0;
         r.c = 0;
-        r.d = ld16<AUX>(x.d, row * 2u);
+        r.d = NO_D ? 0u : ld16<AUX>(x.d, row * 2u);
     }
     return r;
 }
