@@ -339,17 +339,20 @@ def prefill_cells(ctx, fmt, seed):
         wbytes = E * rows * q.row_bytes(fmt, n)
         dbytes = E * rows * n * 2
         dv = dense.view(E * rows, n)
-        # producer, floor and a plain write of the same output bytes (the
-        # write ceiling) alternate, three rounds each, medians of 50 calls
-        arms = {"prod": [], "floor": [], "write": []}
+        # producer, floor and plain writes of the same output bytes (the
+        # write ceiling: one 1 KiB store per wave; and the producer's own
+        # store shape, eight per wave) alternate, three rounds each, medians
+        # of 50 calls
+        arms = {"prod": [], "floor": [], "write": [], "write8": []}
         for _ in range(3):
             arms["prod"].append(timed_eager(torch, lambda i: q.dequant(w, ctx.values, grid, torch.bfloat16, out=dv),
                                             PREFILL_REPS, 2))
             arms["floor"].append(timed_eager(torch, lambda i: q.floor_dequant(w, torch.bfloat16, out=dv),
                                              PREFILL_REPS, 2))
             arms["write"].append(timed_eager(torch, lambda i: q.stream_write(dv, 0x3F803F80), PREFILL_REPS, 2))
+            arms["write8"].append(timed_eager(torch, lambda i: q.stream_write(dv, 0x3F803F80, runs=8), PREFILL_REPS, 2))
         prod_ms, floor_ms = float(np.median(arms["prod"])), float(np.median(arms["floor"]))
-        write_ms = float(np.median(arms["write"]))
+        write_ms, write8_ms = float(np.median(arms["write"])), float(np.median(arms["write8"]))
         q.dequant(w, ctx.values, grid, torch.bfloat16, out=dv)  # the floor left raw words in the dense copy
         pbytes = wbytes + dbytes
         pg = pbytes / (prod_ms * 1e-3) / 1e9
@@ -359,7 +362,9 @@ def prefill_cells(ctx, fmt, seed):
                     "ratio_to_floor": round(prod_ms / floor_ms, 3),
                     "write_ceiling_us": round(write_ms * 1e3, 1),
                     "write_ceiling_GBps": round(dbytes / (write_ms * 1e-3) / 1e9, 1),
-                    "vs_write_ceiling": round(write_ms / prod_ms, 3)})
+                    "vs_write_ceiling": round(write_ms / prod_ms, 3),
+                    "same_shape_write_us": round(write8_ms * 1e3, 1),
+                    "vs_same_shape_write": round(write8_ms / prod_ms, 3)})
         gemm_ms = timed_eager(torch, lambda i: q.grouped_gemm(dense, x, T, K, offsets, perm, x_slots=slots, y=y),
                               PREFILL_REPS, 2)
         gbytes = dbytes + x.numel() * 2 + y.numel() * 4
@@ -749,9 +754,10 @@ def cpu_baseline(oracle, q, synth, gate_up, down, xv, hv, ids_host, bytes_steps,
 
 def write_ceiling(ctx, seed):
     """Plain streaming writes (iqk_stream_write: 16-byte non-temporal stores,
-    1 KiB per wave instruction, the producer's launch shape) of 1.07, 2.15,
-    4.29 and 8.59 GB, then the bf16 producer of each member on the two
-    projection sizes, timed the same way (medians of three rounds of 50
+    1 KiB per wave instruction; one run per wave, and eight, the bf16
+    producer's store shape) of 1.07, 2.15, 4.29 and 8.59 GB, then the bf16
+    producer of each member on the two projection sizes with both writes of
+    its output size, timed the same way (medians of three rounds of 50
     calls).  One JSON line per row."""
     import synth
     q, torch = ctx.q, ctx.torch
@@ -759,11 +765,12 @@ def write_ceiling(ctx, seed):
     buf = torch.empty(E * 2 * I * H * 2, dtype=torch.uint8, device="cuda")  # 8.59 GB: gate/up's dense bf16
     for gb_bytes in (buf.numel() // 8, buf.numel() // 4, buf.numel() // 2, buf.numel()):
         v = buf[:gb_bytes]
-        ms = float(np.median([timed_eager(torch, lambda i: q.stream_write(v, 0x3F803F80), PREFILL_REPS, 2)
-                              for _ in range(3)]))
-        rows.append({"ceiling": "plain write", "bytes": int(gb_bytes), "us": round(ms * 1e3, 1),
-                     "GBps": round(gb_bytes / (ms * 1e-3) / 1e9, 1)})
-        log(json.dumps(rows[-1]))
+        for runs in (1, 8):
+            ms = float(np.median([timed_eager(torch, lambda i: q.stream_write(v, 0x3F803F80, runs=runs),
+                                              PREFILL_REPS, 2) for _ in range(3)]))
+            rows.append({"ceiling": f"plain write, {runs} run(s) per wave", "bytes": int(gb_bytes),
+                         "us": round(ms * 1e3, 1), "GBps": round(gb_bytes / (ms * 1e-3) / 1e9, 1)})
+            log(json.dumps(rows[-1]))
     for fmt in (q.IQ2_K, q.IQ2_KS, q.IQ1_S_R4):
         grid = ctx.grid if fmt == q.IQ1_S_R4 else None
         for proj, (out, n) in (("gate_up", (2 * I, H)), ("down", (H, I))):
@@ -774,12 +781,16 @@ def write_ceiling(ctx, seed):
                                               PREFILL_REPS, 2) for _ in range(3)]))
             wms = float(np.median([timed_eager(torch, lambda i: q.stream_write(dv, 0x3F803F80), PREFILL_REPS, 2)
                                    for _ in range(3)]))
+            w8ms = float(np.median([timed_eager(torch, lambda i: q.stream_write(dv, 0x3F803F80, runs=8),
+                                                PREFILL_REPS, 2) for _ in range(3)]))
             wb = E * out * n * 2
             rb = E * out * q.row_bytes(fmt, n)
             rows.append({"producer": f"{FMT_NAME[fmt]} {proj} bf16", "us": round(ms * 1e3, 1),
                          "bytes": int(wb + rb), "GBps": round((wb + rb) / (ms * 1e-3) / 1e9, 1),
                          "write_ceiling_us": round(wms * 1e3, 1),
-                         "vs_write_ceiling": round(wms / ms, 3)})
+                         "vs_write_ceiling": round(wms / ms, 3),
+                         "same_shape_write_us": round(w8ms * 1e3, 1),
+                         "vs_same_shape_write": round(w8ms / ms, 3)})
             log(json.dumps(rows[-1]))
             del w
             torch.cuda.empty_cache()

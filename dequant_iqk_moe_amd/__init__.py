@@ -97,7 +97,7 @@ def _load():
         "iqk_floor_gemv": (i32, [W, p, p, p, i32, i32, p, i64, i32, p, p]),
         "iqk_floor_dequant": (i32, [W, i64, i64, i32, p, p]),
         "iqk_stream_read": (i32, [p, sz, p, sz, p]),
-        "iqk_stream_write": (i32, [p, sz, ctypes.c_uint32, p]),
+        "iqk_stream_write": (i32, [p, sz, ctypes.c_uint32, i32, p]),
         "iqk_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -422,11 +422,12 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> torch.Ten
     return sink
 
 
-def stream_write(buf: torch.Tensor, value: int = 0, stream=None) -> torch.Tensor:
+def stream_write(buf: torch.Tensor, value: int = 0, runs: int = 1, stream=None) -> torch.Tensor:
     """Plain streaming write of `value` into every 32-bit word of buf (the
-    write ceiling of the dequantization producer)."""
+    write ceiling of the dequantization producer); each wave writes `runs`
+    consecutive 1 KiB runs (1: the fastest shape, 8: the bf16 producer's)."""
     nbytes = buf.numel() * buf.element_size()
-    _check(_lib.iqk_stream_write(_dev(buf, "buf"), nbytes, int(value) & 0xFFFFFFFF, _stream(stream)))
+    _check(_lib.iqk_stream_write(_dev(buf, "buf"), nbytes, int(value) & 0xFFFFFFFF, int(runs), _stream(stream)))
     return buf
 
 

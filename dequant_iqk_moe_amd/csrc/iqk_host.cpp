@@ -476,9 +476,9 @@ int iqk_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_w
     return ok();
 }
 
-int iqk_stream_write(void* buf, size_t bytes, uint32_t value, void* stream) {
-    if (!buf || bytes == 0 || bytes % 16) return fail(IQK_E_ARG, "bad stream-write arguments");
-    hipError_t e = iqk::launch_stream_write(buf, bytes, value, (hipStream_t)stream);
+int iqk_stream_write(void* buf, size_t bytes, uint32_t value, int runs, void* stream) {
+    if (!buf || bytes == 0 || bytes % 16 || runs < 1 || runs > 16) return fail(IQK_E_ARG, "bad stream-write arguments");
+    hipError_t e = iqk::launch_stream_write(buf, bytes, value, runs, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "stream write launch");
     return ok();
 }

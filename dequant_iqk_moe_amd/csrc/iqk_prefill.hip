@@ -317,28 +317,30 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
 
 // plain streaming write (HBM write-ceiling reference): the value in every
 // 16-byte word, non-temporal 16-byte stores, a wave covering 1 KiB per store
-// instruction as the dequantization producer's stores do; each workgroup
-// writes one contiguous span of `per_block` words
-__global__ __launch_bounds__(256) void stream_write_kernel(u32x4* __restrict__ buf, int64_t n16, int64_t per_block,
+// instruction; each wave writes `runs` consecutive 1 KiB runs, the waves of
+// a workgroup adjacent spans.  One run per wave is the fastest plain write
+// measured on this part (6.7 TB/s over 8.6 GB, against 5.3-5.9 TB/s for
+// eight or more stores per wave in any order tried); eight runs per wave is
+// the store shape of the bf16 dequantization producer.
+__global__ __launch_bounds__(256) void stream_write_kernel(u32x4* __restrict__ buf, int64_t n16, int runs,
                                                            uint32_t value) {
-    const int64_t b0 = (int64_t)blockIdx.x * per_block;
-    const int64_t b1 = b0 + per_block < n16 ? b0 + per_block : n16;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t w0 = ((int64_t)blockIdx.x * 4 + wave) * runs * 64;
     const u32x4 v = {value, value, value, value};
-    for (int64_t i = b0 + threadIdx.x; i < b1; i += 256) __builtin_nontemporal_store(v, buf + i);
+    for (int r = 0; r < runs; ++r) {
+        const int64_t i = w0 + (int64_t)r * 64 + lane;
+        if (i < n16) __builtin_nontemporal_store(v, buf + i);
+    }
 }
 
 }  // namespace
 
-hipError_t launch_stream_write(void* buf, size_t bytes, uint32_t value, hipStream_t s) {
+hipError_t launch_stream_write(void* buf, size_t bytes, uint32_t value, int runs, hipStream_t s) {
     const int64_t n16 = (int64_t)(bytes / 16);
-    // the producer's launch cap; each block's span a whole number of 4 KiB runs
-    int64_t blocks = (n16 + 255) / 256;
-    blocks = blocks < 256 * 512 ? blocks : 256 * 512;
-    if (blocks < 1) blocks = 1;
-    const int64_t per_block = ((n16 + blocks - 1) / blocks + 255) / 256 * 256;
-    blocks = (n16 + per_block - 1) / per_block;
-    hipLaunchKernelGGL(stream_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (u32x4*)buf, n16, per_block,
-                       value);
+    const int64_t per_block = (int64_t)256 * runs;  // 16-byte words per workgroup
+    const int64_t blocks = (n16 + per_block - 1) / per_block;
+    if (blocks < 1 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(stream_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (u32x4*)buf, n16, runs, value);
     return hipGetLastError();
 }
 

@@ -333,8 +333,12 @@ int iqk_floor_dequant(const iqk_weights* w, int64_t row0, int64_t nrows, int out
 int iqk_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, void* stream);
 /* Plain HBM streaming write (the write ceiling the dequantization producer
  * is measured against): `value` in every 32-bit word of `bytes` (a
- * multiple of 16) of device memory at `buf`, non-temporal 16-byte stores. */
-int iqk_stream_write(void* buf, size_t bytes, uint32_t value, void* stream);
+ * multiple of 16) of device memory at `buf`, non-temporal 16-byte stores,
+ * 1 KiB per wave and store instruction.  Each wave writes `runs` (1..16)
+ * consecutive 1 KiB runs: 1 gives the highest plain write rate, 8 the store
+ * shape of the bf16 producer (each wave stores the 8 KiB it decoded).
+ * Other values of `runs` fail with IQK_E_ARG. */
+int iqk_stream_write(void* buf, size_t bytes, uint32_t value, int runs, void* stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* iqk_last_error(void);

@@ -160,6 +160,10 @@ def test_validation_errors_before_any_launch():
     w = _wdesc(K, 4, 64, 1024)
     assert L.iqk_moe_gemv_grouped(ctypes.byref(w), vp, None, fake, 2, 1, fake, 1, 6, 0, fake, 1 << 20, fake,
                                   s0) == q._E_WIDTH
+    # plain streaming write: sizes in 16 bytes, 1..16 runs per wave
+    assert L.iqk_stream_write(fake, 100, 0, 1, s0) == q._E_ARG
+    assert L.iqk_stream_write(fake, 4096, 0, 0, s0) == q._E_ARG
+    assert L.iqk_stream_write(fake, 4096, 0, 17, s0) == q._E_ARG
 
 
 def test_python_errors_map_to_exception_types():
