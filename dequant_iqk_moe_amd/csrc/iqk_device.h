@@ -96,6 +96,7 @@ __device__ __forceinline__ ExpertRes expert_res(const P& p, int e) {
     const uint32_t rows = valid ? (uint32_t)p.out : 0u;
     const uint8_t* S = p.S;
     ExpertRes r;
+    r.dp = nullptr;  // (IQ2_K has no per-row scale)
     r.dmax = (uint32_t)p.out - 1u;
     r.q = make_rsrc(S + p.off0 + row0 * St::QS, rows * St::QS);
     r.a = make_rsrc(S + p.off1 + row0 * St::P1, rows * St::P1);
