@@ -306,3 +306,18 @@ def test_floor_and_stream_kernels_run():
     q.stream_read(buf, sk)
     torch.cuda.synchronize()
     assert not torch.any(sink == -7).item()
+
+
+@pytest.mark.parametrize("runs", [1, 8, 16])
+def test_stream_write_fills_exactly_its_buffer(runs):
+    """every 16-byte word of the buffer written, none past it, also for a
+    size that ends inside a workgroup's span"""
+    announce(f"stream write runs={runs}")
+    words = 256 * runs * 5 + 4 * 37  # 16-byte words: five full workgroups and a ragged tail
+    guard = 256
+    buf = torch.zeros((words + guard) * 4, dtype=torch.int32, device="cuda")
+    q.stream_write(buf[:words * 4], 0x3F803F80, runs=runs)
+    torch.cuda.synchronize()
+    h = buf.cpu().numpy().view(np.uint32)
+    assert np.all(h[:words * 4] == 0x3F803F80)
+    assert np.all(h[words * 4:] == 0)
