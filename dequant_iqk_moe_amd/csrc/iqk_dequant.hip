@@ -531,8 +531,12 @@ hipError_t launch_wide(DequantParams p, hipStream_t s) {
     p.ipr = p.n / kWideChunk;
     const int64_t chunks = p.nrows * p.ipr;
     constexpr int64_t kPerThread = FMT == IQK_IQ1_S_R4 && !FLOOR ? IQK_DEQUANT_GRID_CHUNKS : 1;
+    // IQ2_K: one chunk per lane up to twice the usual cap (its 4096-wide
+    // gate/up rows 1712 -> 1622 us with one pass instead of two; IQ2_KS
+    // measured 3 % slower that way, IQ1_S_R4 unchanged)
+    const int64_t cap = FMT == IQK_IQ2_K ? 2 * (int64_t)IQK_DEQUANT_MAX_BLOCKS : (int64_t)IQK_DEQUANT_MAX_BLOCKS;
     int64_t blocks = (chunks + kPerThread * kThreads - 1) / (kPerThread * kThreads);
-    blocks = blocks < IQK_DEQUANT_MAX_BLOCKS ? blocks : IQK_DEQUANT_MAX_BLOCKS;
+    blocks = blocks < cap ? blocks : cap;
     if (blocks < 1) blocks = 1;
     const int64_t stride = blocks * kThreads;
     p.step_row = stride / p.ipr;
