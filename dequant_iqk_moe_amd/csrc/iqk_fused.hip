@@ -136,50 +136,92 @@ struct Table8 {
 // 2-bit members: fragment 2i + h holds weights (4h + d, 4h + d + 8) of code
 // word i as dword d; IQ1_S_R4: fragment 2b + j holds group j of block b in
 // natural order.
-template <int FMT, class Emit>
+// PAIR_SHIFT (2-bit members): the codes of two words shifted together by one
+// 64-bit shift per step (the bits crossing from the high word into the low
+// one land outside every byte's 0x06 mask); measured at 512 tokens: IQ2_K
+// down 245 -> 233 us, IQ2_KS gate/up 461 -> 447 us and down 237 -> 230 us,
+// IQ2_K gate/up 0.6 % slower (it keeps one shift per word).
+template <int FMT, bool PAIR_SHIFT, class Emit>
 __device__ __forceinline__ void decode_chunk(const RowData& r, int c, const Table8& tv, const uint2* grid_s,
                                              Emit emit) {
     const float d = half_to_float(r.d);
     if constexpr (FMT == IQK_IQ2_K || FMT == IQK_IQ2_KS) {
         const uint32_t q[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
-        PairTab t{0u, 0u};
+        auto table_of = [&](int i) {
+            int si;
+            bool alpha;
+            if constexpr (FMT == IQK_IQ2_K) {
+                si = __builtin_amdgcn_sbfe((int)(r.a ^ 0x8888u), 4 * i, 4);  // nibble - 8
+                alpha = (r.b >> (4 * (c & 1) + i)) & 1u;
+            } else {
+                const int j = i >> 1;  // 32-weight sub-block
+                const int sh = 2 * (c & 3) + j;
+                si = (int)(((r.a >> (4 * j)) & 15u) | (((r.b >> sh) & 1u) << 4)) - 16;
+                alpha = (r.c >> sh) & 1u;
+            }
+            const float s = d * (float)si;
+            // alphabet select as one v_bfi_b32 per value (written as C the
+            // compiler makes it two instructions, or a private-memory lookup)
+            const uint32_t m = 0u - (uint32_t)alpha;
+            auto pick = [&](float lo, float hi) {
+                float r;
+                asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(hi), "v"(lo));
+                return r;
+            };
+            return make_pair_tab(s * pick(tv.v0, tv.v4), s * pick(tv.v1, tv.v5), s * pick(tv.v2, tv.v6),
+                                 s * pick(tv.v3, tv.v7));
+        };
+        if constexpr (!PAIR_SHIFT) {
+            PairTab t{0u, 0u};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (FMT == IQK_IQ2_K || (i & 1) == 0) {  // IQ2_KS: one table per two code words
-                int si;
-                bool alpha;
-                if constexpr (FMT == IQK_IQ2_K) {
-                    si = __builtin_amdgcn_sbfe((int)(r.a ^ 0x8888u), 4 * i, 4);  // nibble - 8
-                    alpha = (r.b >> (4 * (c & 1) + i)) & 1u;
-                } else {
-                    const int j = i >> 1;  // 32-weight sub-block
-                    const int sh = 2 * (c & 3) + j;
-                    si = (int)(((r.a >> (4 * j)) & 15u) | (((r.b >> sh) & 1u) << 4)) - 16;
-                    alpha = (r.c >> sh) & 1u;
+            for (int i = 0; i < 4; ++i) {
+                if (FMT == IQK_IQ2_K || (i & 1) == 0) t = table_of(i);  // IQ2_KS: one table per two code words
+                u32x4 f0, f1;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    // bytes of v2: twice the codes of weights jj, 4 + jj, 8 + jj, 12 + jj
+                    const uint32_t v2 = (jj == 0 ? q[i] << 1 : q[i] >> (2 * jj - 1)) & 0x06060606u;
+                    const uint32_t v2p = v2 | 0x01010101u;
+                    f0[jj] = pair_lookup(t, v2, v2p, sel_pair(0, 2));  // (jj, 8 + jj)
+                    f1[jj] = pair_lookup(t, v2, v2p, sel_pair(1, 3));  // (4 + jj, 12 + jj)
                 }
-                const float s = d * (float)si;
-                // alphabet select as one v_bfi_b32 per value (written as C the
-                // compiler makes it two instructions, or a private-memory lookup)
-                const uint32_t m = 0u - (uint32_t)alpha;
-                auto pick = [&](float lo, float hi) {
-                    float r;
-                    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(hi), "v"(lo));
-                    return r;
-                };
-                t = make_pair_tab(s * pick(tv.v0, tv.v4), s * pick(tv.v1, tv.v5), s * pick(tv.v2, tv.v6),
-                             s * pick(tv.v3, tv.v7));
+                emit(2 * i, f0);
+                emit(2 * i + 1, f1);
             }
-            u32x4 f0, f1;
+        } else {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                // bytes of v2: twice the codes of weights jj, 4 + jj, 8 + jj, 12 + jj
-                const uint32_t v2 = (jj == 0 ? q[i] << 1 : q[i] >> (2 * jj - 1)) & 0x06060606u;
-                const uint32_t v2p = v2 | 0x01010101u;
-                f0[jj] = pair_lookup(t, v2, v2p, sel_pair(0, 2));  // (jj, 8 + jj)
-                f1[jj] = pair_lookup(t, v2, v2p, sel_pair(1, 3));  // (4 + jj, 12 + jj)
+            for (int ip = 0; ip < 4; ip += 2) {
+                // the codes of two words shifted together: one 64-bit shift per
+                // step (bits crossing from the high word into the low one land
+                // outside the 0x06 mask of every byte)
+                const uint64_t qq = ((uint64_t)q[ip + 1] << 32) | q[ip];
+                uint32_t lo[4], hi[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    uint64_t sq;
+                    if (jj == 0) asm("v_lshlrev_b64 %0, 1, %1" : "=v"(sq) : "v"(qq));
+                    else asm("v_lshrrev_b64 %0, %1, %2" : "=v"(sq) : "i"(2 * jj - 1), "v"(qq));
+                    lo[jj] = (uint32_t)sq;
+                    hi[jj] = (uint32_t)(sq >> 32);
+                }
+                PairTab t = table_of(ip);  // IQ2_KS: one table for both words
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const int i = ip + h2;
+                    if (FMT == IQK_IQ2_K && h2 == 1) t = table_of(i);
+                    u32x4 f0, f1;
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        // bytes of v2: twice the codes of weights jj, 4 + jj, 8 + jj, 12 + jj
+                        const uint32_t v2 = (h2 ? hi[jj] : lo[jj]) & 0x06060606u;
+                        const uint32_t v2p = v2 | 0x01010101u;
+                        f0[jj] = pair_lookup(t, v2, v2p, sel_pair(0, 2));  // (jj, 8 + jj)
+                        f1[jj] = pair_lookup(t, v2, v2p, sel_pair(1, 3));  // (4 + jj, 12 + jj)
+                    }
+                    emit(2 * i, f0);
+                    emit(2 * i + 1, f1);
+                }
             }
-            emit(2 * i, f0);
-            emit(2 * i + 1, f1);
         }
     } else {
 #pragma unroll
@@ -335,6 +377,7 @@ __device__ __forceinline__ void fused_pass(const FusedParams& p, FusedShared<FMT
                                            const Table8& tv, int base, int M, int tb,
                                            int rb0, int rb1, int tid, int li, int g, int wave, bool nan_out) {
     constexpr int KC = MT == 1 ? (N < kFKC1 ? N : kFKC1) : (N < 2048 ? N : 2048);
+    constexpr bool kPairShift = FMT == IQK_IQ2_KS || N <= 2048;
     constexpr int PITCH = 2 * KC + kFPad;  // LDS row pitch
     constexpr int SSC = KC / 512;          // super-steps per chunk
     // super-steps in flight (IQ2_KS: one, since two spill at k = 4096)
@@ -370,11 +413,11 @@ __device__ __forceinline__ void fused_pass(const FusedParams& p, FusedShared<FMT
                                                                  __builtin_bit_cast(bf16x8, b), acc[m], 0, 0, 0);
             }
         };
-        decode_chunk<FMT>(half_of<FMT, 0>(rp), c0, tv, sh.grid, [&](int mi, const u32x4& b) __attribute__((always_inline)) { mma(arow, mi, b); });
+        decode_chunk<FMT, kPairShift>(half_of<FMT, 0>(rp), c0, tv, sh.grid, [&](int mi, const u32x4& b) __attribute__((always_inline)) { mma(arow, mi, b); });
         // IQ1_S_R4: keep the scheduler from hoisting the second half's grid
         // and activation reads over the first half (it runs out of registers)
         if constexpr (FMT == IQK_IQ1_S_R4 && N != 4096) __builtin_amdgcn_sched_barrier(0);
-        decode_chunk<FMT>(half_of<FMT, 1>(rp), c0 + 1, tv, sh.grid,
+        decode_chunk<FMT, kPairShift>(half_of<FMT, 1>(rp), c0 + 1, tv, sh.grid,
                           [&](int mi, const u32x4& b) __attribute__((always_inline)) { mma(arow + 512, mi, b); });
     };
     auto write_xoff = [&]() __attribute__((always_inline)) {
