@@ -23,12 +23,12 @@
 //   * Per sub-block (16 weights for IQ2_K, 32 for IQ2_KS, 32 for IQ1_S_R4)
 //     the lane builds a 4-entry bf16 table of its possible weights
 //     (scale * table value, or scale * (grid value + shift)); each bf16 pair
-//     of a fragment is then one v_perm_b32 of that table, its selector one
-//     v_perm_b32 of code bytes (2-bit members: the table as two packed bf16
-//     pairs and selector bytes 2c, 2c + 1; IQ1_S_R4, whose codes come from
-//     grid bytes: the table split into low and high bytes and selector bytes
-//     c, 4 + c).  About 2-3 VALU instructions per weight, once per weight
-//     whatever the number of tokens.
+//     of a fragment is then one v_perm_b32 of that table (two packed bf16
+//     pairs), its selector one v_perm_b32 of doubled code bytes 2c and
+//     2c + 1 (2-bit members: shifted and masked out of the code words;
+//     IQ1_S_R4: its grid staged in LDS as doubled codes).  About 2-3 VALU
+//     instructions per weight, once per weight whatever the number of
+//     tokens.
 //   * The expert's token rows (gathered through the routing permutation)
 //     are staged in LDS (all of k for up to 16 tokens, 2048 k at a time for
 //     up to 32), already in
@@ -91,24 +91,10 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// 4-entry bf16 table of one sub-block, split by byte: `lo` holds the low
-// bytes of the four values, `hi` the high bytes.  A pair of weights with
-// codes (a, b) is then perm(hi, lo, [a, 4 + a, b, 4 + b]).
-struct Tab {
-    uint32_t lo, hi;
-};
-__device__ __forceinline__ Tab make_tab(float v0, float v1, float v2, float v3) {
-    const uint32_t p0 = pk_bf16(v0, v1), p1 = pk_bf16(v2, v3);
-    return Tab{__builtin_amdgcn_perm(p1, p0, 0x06040200u), __builtin_amdgcn_perm(p1, p0, 0x07050301u)};
-}
-
-// Selector [c_x, 4 + c_x, c_y, 4 + c_y] from code bytes x, y of v (v4 = v + 4
-// in every byte; byte 4 + i of the perm source is byte i of v4).
+// Selector picking bytes x and y of a word v and of a second word (bytes
+// 4 + i of the perm source): [x, 4 + x, y, 4 + y].
 constexpr uint32_t sel_pair(int x, int y) {
     return (uint32_t)x | (uint32_t)(4 + x) << 8 | (uint32_t)y << 16 | (uint32_t)(4 + y) << 24;
-}
-__device__ __forceinline__ uint32_t table_pair(const Tab& t, uint32_t v, uint32_t v4, uint32_t sel) {
-    return __builtin_amdgcn_perm(t.hi, t.lo, __builtin_amdgcn_perm(v4, v, sel));
 }
 
 // A 4-entry bf16 table kept as two packed pairs (value c at bytes 2c and
@@ -230,19 +216,18 @@ __device__ __forceinline__ void decode_chunk(const RowData& r, int c, const Tabl
             const float s = d * (float)(2 * ((h16 >> 12) & 7u) + 1);
             const float delta = (h16 >> 15) ? -0.125f : 0.125f;
             // entry 0: grid 0, 1: grid +1, 3: grid -1 (grid byte & 3)
-            const Tab t = make_tab(s * delta, s * (1.0f + delta), 0.0f, s * (delta - 1.0f));
+            const PairTab t = make_pair_tab(s * delta, s * (1.0f + delta), 0.0f, s * (delta - 1.0f));
             const uint32_t qsw = b == 0 ? r.q.x : r.q.y;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t idx = ((qsw >> (8 * j)) & 0xFFu) | (((h16 >> (3 * j)) & 7u) << 8);
-                const uint2 gv = grid_s[idx];
-                const uint32_t v0 = gv.x & 0x03030303u, v1 = gv.y & 0x03030303u;
-                const uint32_t v04 = v0 + 0x04040404u, v14 = v1 + 0x04040404u;
+                const uint2 gv = grid_s[idx];  // doubled codes, staged that way
+                const uint32_t v0p = gv.x | 0x01010101u, v1p = gv.y | 0x01010101u;
                 u32x4 f;
-                f[0] = table_pair(t, v0, v04, sel_pair(0, 1));
-                f[1] = table_pair(t, v0, v04, sel_pair(2, 3));
-                f[2] = table_pair(t, v1, v14, sel_pair(0, 1));
-                f[3] = table_pair(t, v1, v14, sel_pair(2, 3));
+                f[0] = pair_lookup(t, gv.x, v0p, sel_pair(0, 1));
+                f[1] = pair_lookup(t, gv.x, v0p, sel_pair(2, 3));
+                f[2] = pair_lookup(t, gv.y, v1p, sel_pair(0, 1));
+                f[3] = pair_lookup(t, gv.y, v1p, sel_pair(2, 3));
                 emit(4 * b + j, f);
             }
         }
@@ -557,9 +542,12 @@ __global__ __launch_bounds__(kFThreads) void fused_prefill_kernel(FusedParams p)
 
     uint32_t off_grid = 0;
     if constexpr (FMT == IQK_IQ1_S_R4) {
+        // staged as doubled codes (2 (g & 3) per byte: the byte offset of
+        // the grid value's bf16 in a pair table)
         for (int i = tid; i < 1024; i += kFThreads) {
             const uint4 v = ((const uint4*)p.grid)[i];
-            ((uint4*)sh.grid)[i] = v;
+            ((uint4*)sh.grid)[i] = make_uint4((v.x & 0x03030303u) << 1, (v.y & 0x03030303u) << 1,
+                                              (v.z & 0x03030303u) << 1, (v.w & 0x03030303u) << 1);
             off_grid |= non_ternary(v.x) | non_ternary(v.y) | non_ternary(v.z) | non_ternary(v.w);
         }
     }
