@@ -167,6 +167,26 @@ def test_gemv_invalid_ids_give_nan_rows():
     assert np.all(rel_err_per_vector(y[0, [0, 3]], ref[0, [0, 3]]) <= TOL_GEMV)
 
 
+@pytest.mark.parametrize("fmt", [KS, R4])
+@pytest.mark.parametrize("n", [2048, 4096])
+def test_gemv_invalid_ids_wide_rows(fmt, n):
+    # the per-row scale of these widths comes through a scalar load from the
+    # expert's plane (expert 0's for an invalid id, clamped rows past the
+    # last): invalid pairs still read NaN and the valid ones stay exact
+    out, E = (68 if fmt == R4 else 70), 3  # IQ2_KS: a ragged last row group
+    _, w, s = _weights(fmt, E, out, n, 520 + n // 1024 + fmt)
+    values = synth.values_table(521)
+    grid = synth.ternary_grid(522)
+    ids = np.array([[0, 7, -1, 2], [2, 1, 5, 0]], np.int32)
+    x = bf16_round(synth.normal((2, 1, n), 523))
+    announce(f"gemv invalid ids fmt={fmt} n={n}")
+    y = q.moe_gemv(w, to_dev(x, torch.bfloat16), to_dev(ids), values, to_dev(grid)).cpu().numpy()
+    bad = (ids < 0) | (ids >= E)
+    assert np.all(np.isnan(y[bad]))
+    ref = oracle.moe(fmt, s, E, out, n, x, np.where(bad, 0, ids).astype(np.int32), values, grid)
+    assert np.all(rel_err_per_vector(y[~bad], ref[~bad]) <= TOL_GEMV)
+
+
 def test_gemv_invalid_ids_inside_multi_pair_blocks():
     # out = 8 rows at n = 512 is one reduction group per pair, so every
     # workgroup spans several pairs; invalid ids must only blank their own
